@@ -1,0 +1,355 @@
+"""Benchmark of the LTE sparse-attention layer on one MI355X.
+
+One step = one pass of the whole hot path on synthetic inputs:
+  * prefill of a B=32 x 4096-token bf16 prompt (Hq16 Hkv4 D128, sink 4, window
+    512, capacity 512, scoring CNN with per-head b2 ~ U(-2, 1)): score, select,
+    attend, build the cache;
+  * 512 decode steps on that cache shape, each step run on L independent layer
+    caches in rotation (L chosen so the caches exceed twice the 256 MB
+    Infinity Cache, like consecutive layers of a model), replayed from a HIP
+    graph.
+Reported: prefill tokens/s (``value``) and decode microseconds per layer-step,
+each with the roofline of its dominant kernel, next to the CPU oracle timed on
+this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
+                       [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LTE layer prefill tokens/s and decode µs/step, B=32, 4K prompt; % of roofline"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
+MALL_BYTES = 256 * 2**20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="sequences the oracle runs for the CPU baseline (0: one per core)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work from the realised masks
+# ---------------------------------------------------------------------------
+
+def visible_counts(rank: np.ndarray, T: int, s: int, w: int, C: int) -> np.ndarray:
+    """|V(i)| per (b, g, i) from the GPU's candidate ranks.
+
+    |R_i| = min(C, N(i - w)) with N(m) the number of candidates <= m (R_i is the
+    top-C of those); the sink adds the tokens [0, s) that are not in the window.
+    """
+    cand = (rank != 0x7FFFFFFF)
+    N = np.cumsum(cand, axis=-1)                             # N(m)
+    i = np.arange(T)
+    Rn = np.zeros(rank.shape, np.int64)
+    m = i - w
+    ok = m >= 0
+    Rn[..., ok] = np.minimum(C, N[..., m[ok]])
+    win = np.minimum(i + 1, w)
+    sink_extra = np.maximum(0, np.minimum(s, i + 1) - np.maximum(0, i - w + 1))
+    return Rn + (win + sink_extra)[None, None, :]
+
+
+def kernel_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(name: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_sha(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on this host's cores
+# ---------------------------------------------------------------------------
+
+def _oracle_worker(args):
+    import threadpoolctl
+    with threadpoolctl.threadpool_limits(1):
+        import oracle
+        q, k, v, cnn, s, w, C = args
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, s, w, C, cnn=cnn)
+        return time.perf_counter() - t0
+
+
+def _oracle_decode_worker(args):
+    import threadpoolctl
+    with threadpoolctl.threadpool_limits(1):
+        import oracle
+        q, k, v, cnn, s, w, C, T, n = args
+        pre = oracle.prefill(q[:, :T], k[:, :T], v[:, :T], s, w, C, cnn=cnn, rows=[])
+        cache = oracle.LayerCache.from_prefill(k[:, :T], v[:, :T], pre["scores"], pre["ends"],
+                                               s, w, C, cnn=cnn)
+        t0 = time.perf_counter()
+        for t in range(T, T + n):
+            cache.step(q[:, t], k[:, t], v[:, t])
+        return (time.perf_counter() - t0) / n
+
+
+def cpu_baseline(inp, wl, T, sample):
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, 16))
+    nseq = sample if sample > 0 else workers
+    nseq = min(nseq, wl.B)
+    nseq0 = min(max(sample, workers), wl.B)
+    q = inp["q"][:nseq0].float().numpy()
+    k = inp["k"][:nseq0].float().numpy()
+    v = inp["v"][:nseq0].float().numpy()
+    cnn = inp["cnn"]
+    jobs = [(q[b:b + 1, :T], k[b:b + 1, :T], v[b:b + 1, :T], cnn, wl.sink, wl.window,
+             wl.capacity) for b in range(nseq)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(min(workers, nseq)) as pool:
+        pool.map(_oracle_worker, jobs)
+    wall = time.perf_counter() - t0
+    used = min(workers, nseq)
+    # decode: a few steps of one sequence per worker
+    ndec = 8
+    djobs = [(q[b:b + 1], k[b:b + 1], v[b:b + 1], cnn, wl.sink, wl.window, wl.capacity, T, ndec)
+             for b in range(used)]
+    with ctx.Pool(used) as pool:
+        per_seq_step = pool.map(_oracle_decode_worker, djobs)
+    # one decode step of the full batch, spread over the same workers
+    dec_us = float(np.mean(per_seq_step)) * math.ceil(wl.B / used) * 1e6
+    return {
+        "value": nseq * T / wall, "unit": "tokens/s", "cores": used, "kind": "oracle",
+        "sample": f"prefill of {nseq} of the {wl.B} sequences (all {wl.Hkv} KV heads, "
+                  f"T={T}), one process per sequence; decode: {ndec} steps of {used} sequences, "
+                  f"scaled to the full batch",
+        "decode_us_per_step": dec_us,
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(batch and KV-head sharding need no communication and are described in the "
+              "design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from learnable_kv_cache_amd import lte, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ndec = args.decode_steps
+    inp = synth.workload_inputs(4, decode_steps=ndec)
+    wl = inp["workload"]
+    B, T = wl.B, inp["T"]
+    cfg = lte.Config(B, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window, wl.capacity)
+    layer = lte.Layer(cfg)
+    q = inp["q"].to(dev)
+    k = inp["k"].to(dev)
+    v = inp["v"].to(dev)
+    qp, kp, vp = (x[:, :T].contiguous() for x in (q, k, v))
+    dq = [q[:, T + t].contiguous() for t in range(ndec)]
+    dk = [k[:, T + t].contiguous() for t in range(ndec)]
+    dv = [v[:, T + t].contiguous() for t in range(ndec)]
+    cnn = lte.CNN(inp["cnn"], dev)
+    ws = layer.alloc_workspace(T, dev)
+    out = torch.empty_like(qp)
+    cache0 = layer.alloc_cache(dev)
+    cache_bytes = layer.cache_bytes()
+    L = math.ceil(2 * MALL_BYTES / cache_bytes) + 1
+    stream = torch.cuda.current_stream()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def prefill_staged():
+        ev[0].record(stream)
+        layer.prefill_score(kp, vp, cnn, ws)
+        ev[1].record(stream)
+        layer.prefill_select(T, ws)
+        ev[2].record(stream)
+        layer.prefill_attend(qp, kp, vp, ws, out)
+        ev[3].record(stream)
+        layer.prefill_build_cache(kp, vp, ws, cache0)
+        ev[4].record(stream)
+
+    prefill_staged()
+    torch.cuda.synchronize()
+
+    caches = [cache0] + [cache0.clone() for _ in range(L - 1)] if not args.no_decode else []
+    dec_out = torch.empty_like(dq[0])
+
+    def decode_loop(cs):
+        for t in range(ndec):
+            for c in cs:
+                layer.decode_step(dq[t], dk[t], dv[t], cnn, c, ws, dec_out)
+
+    graphs = {}
+    if not args.no_decode:
+        warm_caches = [caches[0]]
+        for name, cs in (("rotating", caches), ("warm", warm_caches)):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for c in cs:
+                    layer.decode_step(dq[0], dk[0], dv[0], cnn, c, ws, dec_out)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                decode_loop(cs)
+            torch.cuda.synchronize()
+            graphs[name] = g
+
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stage_ms = {"score": [], "select": [], "attend": [], "build_cache": []}
+    prefill_ms, dec_rot_ms, dec_warm_ms, step_ms = [], [], [], []
+    for it in range(args.warmup + args.steps):
+        timed = it >= args.warmup
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        prefill_staged()
+        if not args.no_decode:
+            dev_ev[0].record(stream)
+            graphs["rotating"].replay()
+            dev_ev[1].record(stream)
+            graphs["warm"].replay()
+            dev_ev[2].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if timed:
+            step_ms.append((t1 - t0) * 1e3)
+            stage_ms["score"].append(ev[0].elapsed_time(ev[1]))
+            stage_ms["select"].append(ev[1].elapsed_time(ev[2]))
+            stage_ms["attend"].append(ev[2].elapsed_time(ev[3]))
+            stage_ms["build_cache"].append(ev[3].elapsed_time(ev[4]))
+            prefill_ms.append(ev[0].elapsed_time(ev[4]))
+            if not args.no_decode:
+                dec_rot_ms.append(dev_ev[0].elapsed_time(dev_ev[1]))
+                dec_warm_ms.append(dev_ev[1].elapsed_time(dev_ev[2]))
+
+    # realised masks of the last prefill -> algorithmic work
+    views = layer.workspace_views(ws, T)
+    rank = views["rank"].cpu().numpy()
+    vis = visible_counts(rank, T, wl.sink, wl.window, wl.capacity)       # [B, Hkv, T]
+    G = wl.Hq // wl.Hkv
+    attn_flops = 4.0 * wl.D * G * float(vis.sum())
+    cnn_flops = 2.0 * (3 * 2 * wl.D * 32 + 3 * 32) * B * T * wl.Hkv
+    ncand = views["ncand"].cpu().numpy()
+    cand_rate = ncand / max(1, T - wl.window - wl.sink)
+
+    pf_ms = float(np.mean(prefill_ms))
+    att_ms = float(np.mean(stage_ms["attend"]))
+    achieved = attn_flops / (att_ms * 1e-3)
+    attend_src = os.path.join(ROOT, "learnable_kv_cache_amd", "csrc", "attend.hip")
+    traffic = measured_traffic("attend_prefill", attend_src)
+    roofline = {"bound": "mfma", "kernel": "attend_prefill_kernel<128,4>",
+                "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_FLOPS, "traffic": traffic,
+                "flops_per_launch": attn_flops, "ms_per_launch": att_ms}
+    kv_bytes = 2 * B * T * wl.Hkv * wl.D * 2
+    score_ms = float(np.mean(stage_ms["score"]))
+    stages = {
+        "score": {"ms": score_ms, "bound": "hbm",
+                  "achieved_GBps": kv_bytes / (score_ms * 1e-3) / 1e9,
+                  "frac": kv_bytes / (score_ms * 1e-3) / PEAK_HBM_BPS},
+        "select": {"ms": float(np.mean(stage_ms["select"]))},
+        "attend": {"ms": att_ms, "frac_mfma": achieved / PEAK_BF16_FLOPS},
+        "build_cache": {"ms": float(np.mean(stage_ms["build_cache"]))},
+    }
+    result = {
+        "metric": METRIC,
+        "value": B * T / (pf_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": float(np.mean(step_ms)),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill-b32-t4096 then decode-b32 (512 steps)", "B": B, "T": T,
+                   "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "sink": wl.sink, "window": wl.window,
+                   "capacity": wl.capacity, "decode_steps": ndec, "decode_layers": L},
+        "prefill_ms": pf_ms,
+        "roofline": roofline,
+        "stages": stages,
+        "retention": {"candidate_rate_per_head": [float(x) for x in cand_rate.mean(axis=0)],
+                      "mean_visible_keys_per_row": float(vis.mean()),
+                      "prefill_flops": attn_flops + cnn_flops},
+    }
+    if not args.no_decode:
+        # algorithmic bytes of one layer-step: K and V of every visible key (once per KV
+        # head), q, o, the new k/v, the score scan of a full retained segment
+        cv = layer.cache_views(caches[-1])
+        counts = cv["count"].cpu().numpy()
+        pos = int(cv["pos"].cpu().numpy().max())
+        nvis = float(counts.mean()) + wl.window + wl.sink
+        step_bytes = (B * wl.Hkv * nvis * wl.D * 2 * 2 + 2 * B * wl.Hq * wl.D * 2
+                      + 2 * B * wl.Hkv * wl.D * 2 + B * wl.Hkv * wl.capacity * 4)
+        us_rot = float(np.mean(dec_rot_ms)) * 1e3 / (ndec * L)
+        us_warm = float(np.mean(dec_warm_ms)) * 1e3 / ndec
+        achieved_b = step_bytes / (us_rot * 1e-6)
+        result["decode"] = {
+            "us_per_step": us_rot, "warm_single_cache_us_per_step": us_warm,
+            "layers_rotated": L, "cache_bytes": cache_bytes, "approx_position": pos,
+            "roofline": {"bound": "hbm", "achieved": achieved_b / 1e9,
+                         "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                         "frac": achieved_b / PEAK_HBM_BPS, "bytes_per_step": step_bytes,
+                         "traffic": None},
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, wl, T, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

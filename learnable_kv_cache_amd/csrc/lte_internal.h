@@ -1,0 +1,161 @@
+// Internal declarations shared by the HIP sources of liblte.so.
+//
+// Layout arithmetic (cache blob and workspace), vector types for the gfx950
+// MFMA builtins, and the host-side launchers each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lte.h"
+
+namespace lte {
+
+// ---------------------------------------------------------------------------
+// vector types
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHidden = 32;         // scoring-CNN width
+constexpr int kMaxSink = 256;
+constexpr int kMaxCapacity = 4096;
+constexpr int64_t kMaxT = 32768;     // the selection sort keeps <= 32 keys per thread
+constexpr int32_t kNotCand = 0x7fffffff;   // rank of a non-candidate
+constexpr int32_t kAllPass = 0x7ffffffe;   // thr when every candidate is kept
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Plain copy of lte_config with derived sizes.
+struct Shape {
+    int B, Hq, Hkv, D, s, w, C, G, S;   // S = s + C + w cache slots per (b, g)
+};
+
+inline Shape make_shape(const lte_config& c) {
+    Shape sh;
+    sh.B = c.batch; sh.Hq = c.q_heads; sh.Hkv = c.kv_heads; sh.D = c.head_dim;
+    sh.s = c.sink; sh.w = c.window; sh.C = c.capacity;
+    sh.G = c.kv_heads > 0 ? c.q_heads / c.kv_heads : 0;
+    sh.S = c.sink + c.capacity + c.window;
+    return sh;
+}
+
+// ---------------------------------------------------------------------------
+// cache blob layout
+// ---------------------------------------------------------------------------
+inline lte_cache_layout cache_layout(const Shape& sh) {
+    lte_cache_layout L{};
+    size_t bg = size_t(sh.B) * sh.Hkv;
+    size_t off = 0;
+    L.k = off; off = align256(off + bg * sh.S * sh.D * 2);
+    L.v = off; off = align256(off + bg * sh.S * sh.D * 2);
+    L.ret_idx = off; off = align256(off + bg * size_t(sh.C) * 4);
+    L.ret_score = off; off = align256(off + bg * size_t(sh.C) * 4);
+    L.ring_score = off; off = align256(off + bg * size_t(sh.w) * 4);
+    L.count = off; off = align256(off + bg * 4);
+    L.pos = off; off = align256(off + bg * 8);
+    L.next_unscored = off; off = align256(off + bg * 8);
+    L.flags = off; off = align256(off + bg * 4);
+    L.total = off;
+    return L;
+}
+
+// Device-side view of a cache blob.
+struct CacheView {
+    uint16_t* k;           // [B][Hkv][S][D]
+    uint16_t* v;
+    int32_t* ret_idx;      // [B][Hkv][C]
+    float* ret_score;      // [B][Hkv][C]
+    float* ring_score;     // [B][Hkv][w]
+    int32_t* count;        // [B][Hkv]
+    int64_t* pos;          // [B][Hkv]
+    int64_t* next_unscored;
+    int32_t* flags;
+};
+
+inline CacheView cache_view(const Shape& sh, void* base) {
+    lte_cache_layout L = cache_layout(sh);
+    char* p = static_cast<char*>(base);
+    CacheView c;
+    c.k = reinterpret_cast<uint16_t*>(p + L.k);
+    c.v = reinterpret_cast<uint16_t*>(p + L.v);
+    c.ret_idx = reinterpret_cast<int32_t*>(p + L.ret_idx);
+    c.ret_score = reinterpret_cast<float*>(p + L.ret_score);
+    c.ring_score = reinterpret_cast<float*>(p + L.ring_score);
+    c.count = reinterpret_cast<int32_t*>(p + L.count);
+    c.pos = reinterpret_cast<int64_t*>(p + L.pos);
+    c.next_unscored = reinterpret_cast<int64_t*>(p + L.next_unscored);
+    c.flags = reinterpret_cast<int32_t*>(p + L.flags);
+    return c;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+// Selection works on rank blocks of `rbs` ranks; one cumulative position
+// bitmap ("snapshot") per rank block.
+inline int select_rbs(int64_t T) {
+    int64_t f = (T + 16383) / 16384;
+    return int(64 * (f < 1 ? 1 : f));
+}
+inline int64_t select_nsnap_max(int64_t T) {
+    int rbs = select_rbs(T);
+    return (T + rbs - 1) / rbs;
+}
+inline int64_t select_words(int64_t T) { return (T + 31) / 32; }
+
+// Per-(b, g) scratch of the selection kernel, in 4-byte words.
+inline size_t select_scratch_words(int64_t T) {
+    int64_t Tp = (T + 63) & ~int64_t(63);
+    return size_t(4 * Tp) + align256(size_t(2 * select_nsnap_max(T) * select_words(T)) * 4) / 4;
+}
+
+// Decode split-K: keys per split and the number of splits.
+constexpr int kDecodeSplitKeys = 128;
+inline int decode_nsplit(const Shape& sh) { return (sh.S + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
+
+struct WsLayout {
+    size_t scores, rank, thr, ncand, w1p, select_scratch, dec_part, total;
+};
+
+inline WsLayout ws_layout(const Shape& sh, int64_t T) {
+    WsLayout W{};
+    size_t bg = size_t(sh.B) * sh.Hkv;
+    size_t off = 0;
+    W.scores = off; off = align256(off + bg * size_t(T) * 4);
+    W.rank = off; off = align256(off + bg * size_t(T) * 4);
+    W.thr = off; off = align256(off + bg * size_t(T) * 4);
+    W.ncand = off; off = align256(off + bg * 4);
+    W.w1p = off; off = align256(off + size_t(sh.Hkv) * 3 * (2 * sh.D) * kHidden * 2);
+    W.select_scratch = off; off = align256(off + (T > 0 ? bg * select_scratch_words(T) * 4 : 0));
+    W.dec_part = off;
+    off = align256(off + bg * size_t(decode_nsplit(sh)) * sh.G * (sh.D + 2) * 4);
+    W.total = off;
+    return W;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+hipError_t launch_pack_w1(const Shape& sh, const float* w1, uint16_t* w1p, hipStream_t st);
+hipError_t launch_score_prefill(const Shape& sh, int64_t T, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* w1p, const lte_cnn& cnn, float* scores,
+                                hipStream_t st);
+hipError_t launch_select(const Shape& sh, int64_t T, const float* scores, int32_t* rank,
+                         int32_t* thr, int32_t* ncand, uint32_t* scratch, hipStream_t st);
+hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, const int32_t* rank,
+                                 const int32_t* thr, uint16_t* out, hipStream_t st);
+hipError_t launch_build_cache(const Shape& sh, int64_t T, const uint16_t* k, const uint16_t* v,
+                              const float* scores, const int32_t* rank, const int32_t* thr,
+                              const CacheView& cache, hipStream_t st);
+hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_t st);
+hipError_t launch_score_evict(const Shape& sh, const lte_cnn& cnn, const uint16_t* k_t,
+                              const uint16_t* v_t, const CacheView& cache, hipStream_t st);
+hipError_t launch_decode_attend(const Shape& sh, const uint16_t* q_t, const CacheView& cache,
+                                float* part, uint16_t* out_t, hipStream_t st);
+
+}  // namespace lte

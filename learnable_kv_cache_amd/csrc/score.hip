@@ -1,0 +1,102 @@
+// Retention scoring CNN over a whole prompt on gfx950.
+//
+// LTE paper (arXiv 2510.20787) summary page, Figure 2 caption: a CNN stack
+// reads the keys/values of short-range past and future neighbours and
+// predicts a per-token, per-head retention score r_{j,h}.  Shape used here:
+// per KV head, conv1d(2D -> 32, kernel 3, zero pad 1) over concat(k, v),
+// exact GELU, conv1d(32 -> 1, kernel 3, zero pad 1), sigmoid.  x is bf16
+// (the layer's input dtype), W1 is rounded to bf16, accumulation is fp32; the
+// GELU, the 96-term second layer and the sigmoid run in fp32.
+//
+// Grid: one workgroup per 124 consecutive tokens of one (batch, KV head).
+// Tokens outside [0, T) read as zero (first layer's padding) and their hidden
+// activations are zero (second layer's padding).
+#include "score_core.h"
+
+namespace lte {
+namespace {
+
+// W1 [Hkv][32][2D][3] fp32 -> w1p [Hkv][3][2D/16][64 lanes][8] bf16: the B
+// operand of v_mfma_f32_32x32x16_bf16 for output column o = lane % 32 and
+// input channels c = 16 kk + 8 (lane / 32) + e.
+__global__ void pack_w1_kernel(int Hkv, int D, const float* __restrict__ w1,
+                               __bf16* __restrict__ w1p) {
+    const int KK = (2 * D) / 16;
+    const long total = long(Hkv) * 3 * KK * 64 * 8;
+    for (long x = blockIdx.x * long(blockDim.x) + threadIdx.x; x < total;
+         x += long(gridDim.x) * blockDim.x) {
+        const int e = int(x % 8);
+        int tap, kk, lane;
+        w1p_coords(int((x / 8) % (3L * KK * 64)), KK, tap, kk, lane);
+        const int g = int(x / (8L * 64 * KK * 3));
+        const int o = lane % 32;
+        const int c = kk * 16 + (lane / 32) * 8 + e;
+        w1p[x] = (__bf16)w1[((long(g) * kHidden + o) * (2 * D) + c) * 3 + tap];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void score_prefill_kernel(
+    int T, int Hkv, int ntile, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const bf16x8* __restrict__ w1p, const float* __restrict__ b1, const float* __restrict__ w2,
+    const float* __restrict__ b2, float* __restrict__ scores) {
+    __shared__ __align__(16) unsigned char buf[ScoreSmem<D>::kBytes];
+    __shared__ float w2s[kHidden * 3];
+    constexpr int NW = ScoreSmem<D>::NW;
+
+    const int tid = threadIdx.x;
+    const int bg = blockIdx.x / ntile;
+    const int tile = blockIdx.x % ntile;
+    const int b = bg / Hkv;
+    const int g = bg % Hkv;
+    const int t0 = tile * kScoreTile;
+
+    bf16x8* wl = reinterpret_cast<bf16x8*>(buf);
+    const bf16x8* wsrc = w1p + long(g) * NW;
+    for (int x = tid; x < NW; x += 256) wl[x] = wsrc[x];
+    for (int x = tid; x < kHidden * 3; x += 256) w2s[x] = w2[g * kHidden * 3 + x];
+
+    const long row_stride = long(Hkv) * D;
+    const uint16_t* kb = k + (long(b) * T * Hkv + g) * D;
+    const uint16_t* vb = v + (long(b) * T * Hkv + g) * D;
+    float* out = scores + long(bg) * T;
+    score_chunk<D>(
+        buf, w2s, b1 + g * kHidden, b2[g], t0, 0, T - 1,
+        [&](int x, const uint16_t*& kp, const uint16_t*& vp) {
+            if (x < 0 || x >= T) return false;
+            kp = kb + long(x) * row_stride;
+            vp = vb + long(x) * row_stride;
+            return true;
+        },
+        [&](int x) { return x < 0 || x >= T; },
+        [&](int t, float r) { out[t] = r; });
+}
+
+}  // namespace
+
+hipError_t launch_pack_w1(const Shape& sh, const float* w1, uint16_t* w1p, hipStream_t st) {
+    long total = long(sh.Hkv) * 3 * (2 * sh.D / 16) * 64 * 8;
+    int blocks = int((total + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(pack_w1_kernel, dim3(blocks), dim3(256), 0, st, sh.Hkv, sh.D, w1,
+                       reinterpret_cast<__bf16*>(w1p));
+    return hipGetLastError();
+}
+
+hipError_t launch_score_prefill(const Shape& sh, int64_t T, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* w1p, const lte_cnn& cnn, float* scores,
+                                hipStream_t st) {
+    const int ntile = int((T + kScoreTile - 1) / kScoreTile);
+    dim3 grid(unsigned(long(sh.B) * sh.Hkv * ntile));
+    const bf16x8* wp = reinterpret_cast<const bf16x8*>(w1p);
+    if (sh.D == 128) {
+        hipLaunchKernelGGL(score_prefill_kernel<128>, grid, dim3(256), 0, st, int(T), sh.Hkv,
+                           ntile, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+    } else {
+        hipLaunchKernelGGL(score_prefill_kernel<64>, grid, dim3(256), 0, st, int(T), sh.Hkv,
+                           ntile, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lte

@@ -1,0 +1,189 @@
+"""Prefill parity: the HIP path against the CPU oracle (needs an MI355X).
+
+Scores: |r_gpu - r_oracle| <= 5e-4 (W1 is rounded to bf16 on the GPU; with
+weights of std 0.02 the resulting logit error is ~1e-4 rms).  Keep/evict sets:
+identical except for tokens whose oracle score is within 1e-3 of the 0.5
+threshold or of the top-C cut.  Outputs: within 2e-2 max-abs and 1e-3
+mean-abs of the oracle's attention evaluated on the GPU's realised sets
+(bf16 inputs and outputs, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from learnable_kv_cache_amd import lte, synth
+from tests.parity import (MAX_ABS, MEAN_ABS, gpu_ends, keep_set_mismatches, normalize_ends,
+                          output_errors)
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 5e-4
+
+
+def _dev(t):
+    return t.contiguous().cuda()
+
+
+def run_prefill(B, T, Hq, Hkv, D, s, w, C, q, k, v, cnn=None, override=None, with_cache=False):
+    layer = lte.Layer(lte.Config(B, Hq, Hkv, D, s, w, C))
+    ws = layer.alloc_workspace(T)
+    cache = layer.alloc_cache() if with_cache else None
+    dcnn = lte.CNN(cnn) if cnn is not None else None
+    ov = torch.as_tensor(override).cuda() if override is not None else None
+    out = layer.prefill(_dev(q), _dev(k), _dev(v), cnn=dcnn, score_override=ov, cache=cache,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    views = {n: x.cpu().numpy() for n, x in layer.workspace_views(ws, T).items()}
+    return out.float().cpu().numpy(), views, layer, cache
+
+
+def _ends_all(views, w, T):
+    B, Hkv, _ = views["rank"].shape
+    return np.stack([np.stack([gpu_ends(views["rank"][b, g], views["thr"][b, g], w, T)
+                               for g in range(Hkv)]) for b in range(B)])
+
+
+def _check_sets(r_or, ends_or, ends_g, w, C, pairs):
+    for (b, g) in pairs:
+        bad = keep_set_mismatches(r_or[b, g], ends_or[b, g], ends_g[b, g], w, C)
+        assert not bad, f"keep-set mismatch at (b={b}, g={g}): {bad[:5]}"
+
+
+def _check_rows(q, k, v, s, w, ends_g, out, rows, pairs):
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    ref = oracle.attention(qn, kn, vn, s, w, ends_g, rows=rows, pairs=pairs)
+    G = q.shape[2] // k.shape[2]
+    for (b, g) in pairs:
+        sl = slice(g * G, (g + 1) * G)
+        mx, mean = output_errors(out[b, rows, sl], ref[b, rows, sl])
+        assert mx <= MAX_ABS and mean <= MEAN_ABS, (b, g, mx, mean)
+
+
+def test_tiny_layer_end_to_end():
+    """Tiny layer (B1 T256 Hq4 Hkv2 D64 s2 w32 C16, CNN): every output row."""
+    inp = synth.workload_inputs(1)
+    wl = inp["workload"]
+    q, k, v, cnn = inp["q"], inp["k"], inp["v"], inp["cnn"]
+    T = inp["T"]
+    out, views, _, _ = run_prefill(wl.B, T, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window,
+                                   wl.capacity, q, k, v, cnn=cnn)
+    ref = oracle.prefill(q.float().numpy(), k.float().numpy(), v.float().numpy(), wl.sink,
+                         wl.window, wl.capacity, cnn=cnn)
+    err = np.abs(views["scores"] - ref["scores"]).max()
+    assert err <= SCORE_TOL, err
+    ends_g = _ends_all(views, wl.window, T)
+    pairs = [(0, g) for g in range(wl.Hkv)]
+    _check_sets(ref["scores"], ref["ends"], ends_g, wl.window, wl.capacity, pairs)
+    _check_rows(q, k, v, wl.sink, wl.window, ends_g, out, list(range(T)), pairs)
+    for g in range(wl.Hkv):       # every head keeps at most s + w + C keys per row
+        for i in range(T):
+            assert len(oracle.visible_indices(i, wl.sink, wl.window, ends_g[0, g])) <= \
+                wl.sink + wl.window + wl.capacity
+
+
+SHAPES = [
+    # B, T, Hq, Hkv, D, s, w, C, levels
+    (1, 1, 4, 4, 64, 2, 5, 3, 3),
+    (2, 5, 2, 1, 64, 4, 5, 2, 3),
+    (1, 37, 8, 1, 128, 0, 5, 4, 2),
+    (2, 200, 16, 1, 64, 1, 16, 7, 4),
+    (1, 300, 4, 2, 128, 4, 64, 50, 0),
+    (1, 300, 16, 16, 64, 3, 20, 0, 3),
+    (2, 513, 32, 2, 128, 4, 40, 30, 5),
+    (1, 700, 2, 1, 128, 256, 33, 12, 4),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}T{}Hq{}Hkv{}D{}s{}w{}C{}".format(*s[:8]))
+def test_explicit_scores_exact_sets(shape):
+    """Given scores (with forced ties), keep sets must match exactly and every row agree."""
+    B, T, Hq, Hkv, D, s, w, C, levels = shape
+    q, k, v = synth.make_qkv(B, T, Hq, Hkv, D, seed=77 + T)
+    rng = np.random.default_rng(T)
+    if levels:
+        r = rng.choice(np.linspace(0.3, 0.9, levels), size=(B, Hkv, T)).astype(np.float32)
+    else:
+        r = rng.uniform(0.2, 1.0, size=(B, Hkv, T)).astype(np.float32)
+    out, views, _, _ = run_prefill(B, T, Hq, Hkv, D, s, w, C, q, k, v, override=r)
+    ends_or = oracle.all_ends(r, s, w, C, T)
+    ends_g = _ends_all(views, w, T)
+    np.testing.assert_array_equal(normalize_ends(ends_g, w), normalize_ends(ends_or, w))
+    pairs = [(b, g) for b in range(B) for g in range(Hkv)]
+    _check_rows(q, k, v, s, w, ends_g, out, list(range(T)), pairs)
+
+
+def test_all_kept_is_full_causal_and_none_kept_is_swa():
+    """C >= T with every token kept equals full causal attention; retention 0 equals sink+SWA."""
+    B, T, Hq, Hkv, D, s, w = 1, 160, 4, 2, 64, 2, 16
+    q, k, v = synth.make_qkv(B, T, Hq, Hkv, D, seed=5)
+    ones = np.ones((B, Hkv, T), np.float32)
+    out_all, _, _, _ = run_prefill(B, T, Hq, Hkv, D, s, w, T, q, k, v, override=ones)
+    full = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), 0, T,
+                            np.full((B, Hkv, T), -1))
+    mx, mean = output_errors(out_all, full)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
+    zeros = np.zeros((B, Hkv, T), np.float32)
+    out_none, _, _, _ = run_prefill(B, T, Hq, Hkv, D, s, w, 8, q, k, v, override=zeros)
+    swa = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), s, w,
+                           np.full((B, Hkv, T), -1))
+    mx, mean = output_errors(out_none, swa)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    inp = synth.workload_inputs(1)
+    wl = inp["workload"]
+    a, va, _, _ = run_prefill(wl.B, inp["T"], wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window,
+                              wl.capacity, inp["q"], inp["k"], inp["v"], cnn=inp["cnn"])
+    b, vb, _, _ = run_prefill(wl.B, inp["T"], wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window,
+                              wl.capacity, inp["q"], inp["k"], inp["v"], cnn=inp["cnn"])
+    assert np.array_equal(a, b)
+    for n in va:
+        assert np.array_equal(va[n], vb[n]), n
+
+
+def _sample_rows(T, w, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, w - 1, w, w + 1, T - 1]
+    return sorted(set(fixed + rng.integers(0, T, n).tolist()))
+
+
+def test_artificial_cache_full_size():
+    """Kernel-only workload at full size (B8 T4096 Hq16 Hkv4 D128 s4 w512 C512, 10% random
+    retention): exact keep sets for every head; sampled rows against the oracle."""
+    inp = synth.workload_inputs(2)
+    wl = inp["workload"]
+    T = inp["T"]
+    out, views, _, _ = run_prefill(wl.B, T, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window,
+                                   wl.capacity, inp["q"], inp["k"], inp["v"],
+                                   override=inp["override"])
+    ends_or = oracle.all_ends(inp["override"], wl.sink, wl.window, wl.capacity, T)
+    ends_g = _ends_all(views, wl.window, T)
+    np.testing.assert_array_equal(normalize_ends(ends_g, wl.window),
+                                  normalize_ends(ends_or, wl.window))
+    pairs = [(0, 0), (3, 1), (5, 2), (7, 3)]
+    _check_rows(inp["q"], inp["k"], inp["v"], wl.sink, wl.window, ends_g, out,
+                _sample_rows(T, wl.window), pairs)
+
+
+def test_full_layer_prefill_full_size():
+    """Full prefill at B32 T4096 Hq16 Hkv4 D128 s4 w512 C512 with the CNN and per-head
+    b2 ~ U(-2, 1): all scores, keep sets of every head, sampled output rows."""
+    inp = synth.workload_inputs(3)
+    wl = inp["workload"]
+    T = inp["T"]
+    cnn = inp["cnn"]
+    out, views, _, _ = run_prefill(wl.B, T, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window,
+                                   wl.capacity, inp["q"], inp["k"], inp["v"], cnn=cnn)
+    kn, vn = inp["k"].float().numpy(), inp["v"].float().numpy()
+    r_or = oracle.cnn_scores(kn, vn, cnn["W1"], cnn["b1"], cnn["W2"], cnn["b2"])
+    err = np.abs(views["scores"] - r_or).max()
+    assert err <= SCORE_TOL, err
+    ends_or = oracle.all_ends(r_or, wl.sink, wl.window, wl.capacity, T)
+    ends_g = _ends_all(views, wl.window, T)
+    pairs_all = [(b, g) for b in range(wl.B) for g in range(wl.Hkv)]
+    _check_sets(r_or, ends_or, ends_g, wl.window, wl.capacity, pairs_all)
+    pairs = [(0, 0), (9, 1), (17, 2), (31, 3)]
+    _check_rows(inp["q"], inp["k"], inp["v"], wl.sink, wl.window, ends_g, out,
+                _sample_rows(T, wl.window, seed=3), pairs)
