@@ -39,7 +39,7 @@
  *     LTE_ERR_HIP.  No C++ exception crosses this interface.
  *   - Sequences of a batch have equal length.
  *   - Supported: head_dim in {64, 128}; q_heads / kv_heads in {1, 2, 4, 8,
- *     16}; hidden == 32; window >= 5; 0 <= sink <= 256;
+ *     16}; hidden == 32; 5 <= window <= 32768; 0 <= sink <= 256;
  *     0 <= capacity <= 4096; 1 <= T <= 32768 tokens per prefill.
  */
 #ifndef LTE_H
@@ -96,9 +96,18 @@ typedef struct {
  *   pos         int64 [B][Hkv]     tokens ingested so far (all equal)
  *   next_unscored int64 [B][Hkv]   oldest token still lacking a score
  *   flags       int32 [B][Hkv]     bit 0: a token left the window unscored
+ *   weak        int32 [B][Hkv]     slot of the weakest retained entry (lowest
+ *                                  score, then highest index) while the
+ *                                  segment is full, else -1
+ *   nx_slot     int32 [B][Hkv]     decision for the token that leaves at the
+ *                                  next ingest (token pos-w): the segment
+ *                                  slot it takes, -1 if it is not kept, -2
+ *                                  if it would leave unscored
+ *   nx_score    fp32  [B][Hkv]     that token's score
  *   total       size of the blob in bytes                                */
 typedef struct {
-    size_t k, v, ret_idx, ret_score, ring_score, count, pos, next_unscored, flags, total;
+    size_t k, v, ret_idx, ret_score, ring_score, count, pos, next_unscored, flags, weak, nx_slot,
+        nx_score, total;
 } lte_cache_layout;
 
 /* Byte offsets inside a prefill workspace for T tokens (intermediates that
@@ -132,12 +141,15 @@ int lte_cache_get_layout(const lte_config* cfg, lte_cache_layout* out);
 /* Workspace needed by a T-token prefill and by every decode call.  The
  * workspace is scratch: its contents are undefined between calls, except
  * that the views of lte_workspace_get_layout hold the last prefill's
- * intermediates until the next call that uses the same workspace. */
+ * intermediates until the next prefill into the same workspace.  Decode
+ * calls use only the first lte_workspace_bytes(cfg, 0) bytes, which lie
+ * before those views. */
 size_t lte_workspace_bytes(const lte_config* cfg, int64_t T);
 int lte_workspace_get_layout(const lte_config* cfg, int64_t T, lte_workspace_layout* out);
 
 /* Resets a cache to the empty state: pos = 0, count = 0, every ring score
- * NaN, flags 0.  K/V slots are left as they are (never read while invalid). */
+ * NaN, flags 0, weak -1, nx_slot -1.  K/V slots are left as they are (never
+ * read while invalid). */
 int lte_cache_init(const lte_config* cfg, void* cache, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -196,7 +208,12 @@ int lte_score_evict(const lte_config* cfg, const lte_cnn* cnn, const uint16_t* k
 int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, const void* cache,
                       void* workspace, size_t workspace_bytes, uint16_t* out_t, void* stream);
 
-/* One decode step: lte_score_evict followed by lte_decode_attend. */
+/* One decode step, with the result of lte_score_evict followed by
+ * lte_decode_attend: the splits of the cache are read in their pre-step
+ * state with the new token and the segment slot the leaving token takes
+ * substituted; a second launch merges the partial softmax sums in a fixed
+ * order and then updates the cache.  Calls that use one cache must be
+ * ordered on one stream. */
 int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* k_t,
                     const uint16_t* v_t, const lte_cnn* cnn, void* cache, void* workspace,
                     size_t workspace_bytes, uint16_t* out_t, void* stream);

@@ -20,7 +20,7 @@ int check_cfg(const lte_config* cfg) {
     if (c.head_dim != 64 && c.head_dim != 128) return LTE_ERR_UNSUPPORTED;
     if (!pow2_group(c.q_heads / c.kv_heads)) return LTE_ERR_UNSUPPORTED;
     if (c.hidden != kHidden) return LTE_ERR_UNSUPPORTED;
-    if (c.window < 5 || c.window > (1 << 20)) return LTE_ERR_UNSUPPORTED;
+    if (c.window < 5 || c.window > 32768) return LTE_ERR_UNSUPPORTED;
     if (c.sink > kMaxSink || c.capacity > kMaxCapacity) return LTE_ERR_UNSUPPORTED;
     if (long(c.batch) * c.kv_heads > (1L << 20)) return LTE_ERR_UNSUPPORTED;
     return LTE_OK;
@@ -70,10 +70,7 @@ int check_ws(const Shape& sh, int64_t T, const void* ws, size_t bytes) {
     return LTE_OK;
 }
 
-// Decode workspaces are sized for T = 0 (no prefill intermediates) but use the
-// same offsets as a prefill of length T would; the decode partials sit at the
-// end of whatever region the caller sized.  To keep one rule, decode calls
-// place their partials at the T = 0 offset.
+// Decode partials sit at the start of any workspace, before the prefill views.
 float* dec_part_ptr(const Shape& sh, void* ws) {
     return reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(sh, 0).dec_part);
 }
@@ -238,9 +235,9 @@ int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, const void* ca
     Shape sh = make_shape(*cfg);
     if (workspace == nullptr) return LTE_ERR_INVALID_ARG;
     if (workspace_bytes < ws_layout(sh, 0).total) return LTE_ERR_WORKSPACE;
-    return hip_status(launch_decode_attend(sh, q_t, cache_view(sh, const_cast<void*>(cache)),
-                                           dec_part_ptr(sh, workspace), out_t,
-                                           hipStream_t(stream)));
+    return hip_status(launch_decode(sh, false, q_t, nullptr, nullptr, nullptr,
+                                    cache_view(sh, const_cast<void*>(cache)),
+                                    dec_part_ptr(sh, workspace), out_t, hipStream_t(stream)));
 }
 
 int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* k_t,
@@ -251,8 +248,8 @@ int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* 
     if (!q_t || !k_t || !v_t || !cache || !out_t || !workspace) return LTE_ERR_INVALID_ARG;
     Shape sh = make_shape(*cfg);
     if (workspace_bytes < ws_layout(sh, 0).total) return LTE_ERR_WORKSPACE;
-    LTE_TRY(lte_score_evict(cfg, cnn, k_t, v_t, cache, stream));
-    return lte_decode_attend(cfg, q_t, cache, workspace, workspace_bytes, out_t, stream);
+    return hip_status(launch_decode(sh, true, q_t, k_t, v_t, cnn, cache_view(sh, cache),
+                                    dec_part_ptr(sh, workspace), out_t, hipStream_t(stream)));
 }
 
 int lte_cache_export(const lte_config* cfg, const void* cache, int32_t* ret_idx,

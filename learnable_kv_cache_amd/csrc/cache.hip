@@ -29,6 +29,9 @@ __global__ void cache_init_kernel(int BG, int w, int s, CacheView c) {
         c.pos[x] = 0;
         c.next_unscored[x] = s;
         c.flags[x] = 0;
+        c.weak[x] = -1;
+        c.nx_slot[x] = -1;
+        c.nx_score[x] = 0.0f;
     }
 }
 
@@ -95,11 +98,54 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int T, int s, int w, in
             __syncthreads();
         }
     }
+    // weakest entry of a full segment: lowest score, then highest token index
+    int wx = -1;
+    if (C > 0 && len == C) {
+        __threadfence_block();
+        __syncthreads();
+        float bs = INFINITY;
+        int bt = -1;
+        for (int x = tid; x < C; x += 256) {
+            const float sc = c.ret_score[long(bg) * C + x];
+            const int tk = c.ret_idx[long(bg) * C + x];
+            if (sc < bs || (sc == bs && tk > bt)) { bs = sc; bt = tk; wx = x; }
+        }
+        __shared__ float rs[4];
+        __shared__ int rt[4], rx[4];
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            const float os = __shfl_xor(bs, d, 64);
+            const int ot = __shfl_xor(bt, d, 64);
+            const int ox = __shfl_xor(wx, d, 64);
+            if (os < bs || (os == bs && ot > bt)) { bs = os; bt = ot; wx = ox; }
+        }
+        if (lane == 0) { rs[wave] = bs; rt[wave] = bt; rx[wave] = wx; }
+        __syncthreads();
+        bs = rs[0]; bt = rt[0]; wx = rx[0];
+        for (int q = 1; q < 4; ++q) {
+            if (rs[q] < bs || (rs[q] == bs && rt[q] > bt)) { bs = rs[q]; bt = rt[q]; wx = rx[q]; }
+        }
+    }
     if (tid == 0) {
         c.count[bg] = len;
         c.pos[bg] = T;
         c.next_unscored[bg] = max(T - 2, s);
         c.flags[bg] = 0;
+        c.weak[bg] = wx;
+        // decision for the token T-w that leaves at the first decode step (its
+        // score is final: its right neighbours T-w+1, T-w+2 exist)
+        int nx = -1;
+        float rl = 0.0f;
+        const int jl = T - w;
+        if (jl >= s) {
+            rl = r[jl];
+            if (rl > 0.5f && C > 0) {
+                if (len < C) nx = len;
+                else if (wx >= 0 && rl > c.ret_score[long(bg) * C + wx]) nx = wx;
+            }
+        }
+        c.nx_slot[bg] = nx;
+        c.nx_score[bg] = rl;
     }
 }
 

@@ -59,6 +59,9 @@ inline lte_cache_layout cache_layout(const Shape& sh) {
     L.pos = off; off = align256(off + bg * 8);
     L.next_unscored = off; off = align256(off + bg * 8);
     L.flags = off; off = align256(off + bg * 4);
+    L.weak = off; off = align256(off + bg * 4);
+    L.nx_slot = off; off = align256(off + bg * 4);
+    L.nx_score = off; off = align256(off + bg * 4);
     L.total = off;
     return L;
 }
@@ -74,6 +77,9 @@ struct CacheView {
     int64_t* pos;          // [B][Hkv]
     int64_t* next_unscored;
     int32_t* flags;
+    int32_t* weak;         // [B][Hkv] weakest slot of a full segment, else -1
+    int32_t* nx_slot;      // [B][Hkv] decision for the next leaving token
+    float* nx_score;       // [B][Hkv] its score
 };
 
 inline CacheView cache_view(const Shape& sh, void* base) {
@@ -89,6 +95,9 @@ inline CacheView cache_view(const Shape& sh, void* base) {
     c.pos = reinterpret_cast<int64_t*>(p + L.pos);
     c.next_unscored = reinterpret_cast<int64_t*>(p + L.next_unscored);
     c.flags = reinterpret_cast<int32_t*>(p + L.flags);
+    c.weak = reinterpret_cast<int32_t*>(p + L.weak);
+    c.nx_slot = reinterpret_cast<int32_t*>(p + L.nx_slot);
+    c.nx_score = reinterpret_cast<float*>(p + L.nx_score);
     return c;
 }
 
@@ -113,8 +122,8 @@ inline size_t select_scratch_words(int64_t T) {
     return size_t(4 * Tp) + align256(size_t(2 * select_nsnap_max(T) * select_words(T)) * 4) / 4;
 }
 
-// Decode split-K: keys per split and the number of splits.
-constexpr int kDecodeSplitKeys = 128;
+// Decode split-K: cache slots per workgroup and the number of splits.
+constexpr int kDecodeSplitKeys = 64;
 inline int decode_nsplit(const Shape& sh) { return (sh.S + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
 
 struct WsLayout {
@@ -122,17 +131,18 @@ struct WsLayout {
 };
 
 inline WsLayout ws_layout(const Shape& sh, int64_t T) {
+    // decode partials first: a decode call never overwrites a prefill's views
     WsLayout W{};
     size_t bg = size_t(sh.B) * sh.Hkv;
     size_t off = 0;
+    W.dec_part = off;
+    off = align256(off + bg * size_t(decode_nsplit(sh)) * sh.G * (sh.D + 2) * 4);
     W.scores = off; off = align256(off + bg * size_t(T) * 4);
     W.rank = off; off = align256(off + bg * size_t(T) * 4);
     W.thr = off; off = align256(off + bg * size_t(T) * 4);
     W.ncand = off; off = align256(off + bg * 4);
     W.w1p = off; off = align256(off + size_t(sh.Hkv) * 3 * (2 * sh.D) * kHidden * 2);
     W.select_scratch = off; off = align256(off + (T > 0 ? bg * select_scratch_words(T) * 4 : 0));
-    W.dec_part = off;
-    off = align256(off + bg * size_t(decode_nsplit(sh)) * sh.G * (sh.D + 2) * 4);
     W.total = off;
     return W;
 }
@@ -155,7 +165,10 @@ hipError_t launch_build_cache(const Shape& sh, int64_t T, const uint16_t* k, con
 hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_t st);
 hipError_t launch_score_evict(const Shape& sh, const lte_cnn& cnn, const uint16_t* k_t,
                               const uint16_t* v_t, const CacheView& cache, hipStream_t st);
-hipError_t launch_decode_attend(const Shape& sh, const uint16_t* q_t, const CacheView& cache,
-                                float* part, uint16_t* out_t, hipStream_t st);
+// ingest == false: attention over the cache as it is (lte_decode_attend);
+// ingest == true: one fused decode step (lte_decode_step).
+hipError_t launch_decode(const Shape& sh, bool ingest, const uint16_t* q_t, const uint16_t* k_t,
+                         const uint16_t* v_t, const lte_cnn* cnn, const CacheView& cache,
+                         float* part, uint16_t* out_t, hipStream_t st);
 
 }  // namespace lte

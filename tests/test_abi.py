@@ -98,7 +98,8 @@ def test_cache_layout_matches_the_documented_sections():
     sizes = [("k", bg * S * c.head_dim * 2), ("v", bg * S * c.head_dim * 2),
              ("ret_idx", bg * c.capacity * 4), ("ret_score", bg * c.capacity * 4),
              ("ring_score", bg * c.window * 4), ("count", bg * 4), ("pos", bg * 8),
-             ("next_unscored", bg * 8), ("flags", bg * 4)]
+             ("next_unscored", bg * 8), ("flags", bg * 4), ("weak", bg * 4),
+             ("nx_slot", bg * 4), ("nx_score", bg * 4)]
     off = 0
     for name, n in sizes:
         assert L[name] == off, name
@@ -115,7 +116,7 @@ def test_workspace_layout():
     for T in (1, 100, 4096, 32768):
         W = layer.workspace_layout(T)
         bg = c.batch * c.kv_heads
-        assert W["scores"] == 0
-        assert W["rank"] >= bg * T * 4 and W["thr"] >= W["rank"] + bg * T * 4
+        assert W["rank"] >= W["scores"] + bg * T * 4 and W["thr"] >= W["rank"] + bg * T * 4
+        assert W["scores"] > 0            # decode partials sit before the prefill views
         assert W["total"] == layer.workspace_bytes(T)
         assert layer.workspace_bytes(0) <= W["total"]

@@ -143,3 +143,32 @@ def test_long_context_decode(rho):
     cnn = dict(cnn0, b2=np.full((wl.Hkv,), b2, np.float32))
     run_decode_parity(wl.B, T, n, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window, wl.capacity, q, k,
                       v, cnn, check_b=[0], every=5)
+
+
+def test_fused_step_equals_evict_then_attend():
+    """lte_decode_step (one fused kernel) == lte_score_evict then lte_decode_attend, bitwise,
+    including across a deferred-scoring step and segment overflow."""
+    B, T, n, Hq, Hkv, D, s, w, C = 2, 60, 40, 8, 2, 128, 2, 9, 5
+    q, k, v, cnn = synth.random_case(21, B, T + n, Hq, Hkv, D, b2=0.05)
+    layer = lte.Layer(lte.Config(B, Hq, Hkv, D, s, w, C))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    dcnn = lte.CNN(cnn)
+    ws = layer.alloc_workspace(T)
+    ca, cb = layer.alloc_cache(), layer.alloc_cache()
+    for cache in (ca, cb):
+        layer.prefill(qd[:, :T].contiguous(), kd[:, :T].contiguous(), vd[:, :T].contiguous(),
+                      cnn=dcnn, cache=cache, workspace=ws)
+    for t in range(T, T + n):
+        qt, kt, vt = qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous()
+        oa = layer.decode_step(qt, kt, vt, dcnn, ca, ws)
+        layer.score_evict(kt, vt, dcnn, cb)
+        ob = layer.decode_attend(qt, cb, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), t
+    va, vb = layer.cache_views(ca), layer.cache_views(cb)
+    for name in ("ret_idx", "ret_score", "count", "pos", "next_unscored", "flags", "weak",
+                 "nx_slot", "nx_score"):
+        assert torch.equal(va[name], vb[name]), name
+    # ring scores: NaN where unscored on both sides
+    assert torch.equal(torch.nan_to_num(va["ring_score"], nan=-1.0),
+                       torch.nan_to_num(vb["ring_score"], nan=-1.0))
