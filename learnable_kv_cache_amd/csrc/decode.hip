@@ -101,6 +101,10 @@ __device__ void ingest_finish(const CacheView& c, int bg, int g, int s, int w, i
     const long ring_row = (long(bg) * S + ring0 + tslot) * D;
     const int64_t jl = t - w;
     const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
+    // score of token t+1-w, which leaves at the next ingest: scored at least three
+    // steps before it leaves, never by this step's batch
+    const int64_t t1 = t + 1;
+    const float r1 = (t1 - w >= s) ? c.ring_score[long(bg) * w + int(t1 % w)] : 0.0f;
 
     if (tid < D / 8) {       // same thread reads the ring chunk before overwriting it
         const int ch = tid;
@@ -204,10 +208,7 @@ __device__ void ingest_finish(const CacheView& c, int bg, int g, int s, int w, i
         }
         u2 = t - 1;
     }
-    // the next ingest's decision: token t+1-w, whose score is final by now
-    const int64_t t1 = t + 1;
-    float r1 = 0.0f;
-    if (t1 - w >= s) r1 = c.ring_score[long(bg) * w + int(t1 % w)];
+    // the next ingest's decision
     if (tid == 0) {
         c.nx_slot[bg] = decide_slot(t1, r1, new_cnt, wk2, ws2, s, w, C);
         c.nx_score[bg] = r1;
@@ -291,54 +292,70 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 c.v + base + long(min(slot0 + 4 * kg + k4, S - 1)) * D + 8 * dg);
     }
 
-    // ---- the state, loaded alongside -------------------------------------------------
-    const int64_t p = c.pos[bg];
+    // ---- the state, loaded alongside (positions fit in 32 bits) ----------------------
+    const int p = int(c.pos[bg]);
     const int cnt = c.count[bg];
     const int X = INGEST ? c.nx_slot[bg] : -1;
-    const int64_t t = INGEST ? p : p - 1;
-    const int tslot = t >= 0 ? int(t % w) : 0;
+    const int t = INGEST ? p : p - 1;
+    const int tslot = t >= 0 ? t % w : 0;
     const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
 
     // rows that differ in the post-ingest state: the new token (ring slot t mod w and,
     // while t < s, sink slot t) comes from the inputs; segment slot X holds the leaving
-    // token, still in ring slot t mod w
-    auto fixed_row = [&](int cs, const uint16_t* cache, const uint16_t* in) -> const uint16_t* {
-        if (!INGEST || cs >= S) return nullptr;
-        if (cs < s) return (cs == t) ? in + long(bg) * D : nullptr;
-        if (cs < s + C) return (cs - s == X) ? cache + base + long(s + C + tslot) * D : nullptr;
-        return (cs - s - C == tslot) ? in + long(bg) * D : nullptr;
-    };
+    // token, still in ring slot t mod w.  At most three slots, each checked once.
     if (INGEST) {
+        const int fs[3] = {t < s ? t : -1, X >= 0 ? s + X : -1, s + C + tslot};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const uint16_t* r = fixed_row(slot0 + 16 * mt + l16, c.k, k_t);
-            if (r != nullptr) {
+        for (int f = 0; f < 3; ++f) {
+            const int kk = fs[f] - slot0;                     // wave-uniform
+            if (fs[f] < 0 || kk < 0 || kk >= KPB || fs[f] >= S) continue;
+            const uint16_t* rk = (f == 1) ? c.k + base + long(s + C + tslot) * D : k_t + long(bg) * D;
+            const uint16_t* rv = (f == 1) ? c.v + base + long(s + C + tslot) * D : v_t + long(bg) * D;
+            if (l16 == (kk & 15)) {                           // q.k A operand rows
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk)
-                    ka[mt][kk] = *reinterpret_cast<const bf16x8*>(r + 32 * kk + 8 * q16);
+                for (int mt = 0; mt < 4; ++mt) {
+                    if (mt == (kk >> 4)) {
+#pragma unroll
+                        for (int kq = 0; kq < KS; ++kq)
+                            ka[mt][kq] = *reinterpret_cast<const bf16x8*>(rk + 32 * kq + 8 * q16);
+                    }
+                }
             }
-        }
 #pragma unroll
-        for (int uu = 0; uu < NU; ++uu) {
-            const int U = lane + 64 * uu;
-            const int kg = U / (D / 8);
-            const int dg = U % (D / 8);
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const uint16_t* r = fixed_row(slot0 + 4 * kg + k4, c.v, v_t);
-                if (r != nullptr) vr[uu][k4] = *reinterpret_cast<const uint4*>(r + 8 * dg);
+            for (int uu = 0; uu < NU; ++uu) {                 // V transpose units
+                const int U = lane + 64 * uu;
+                if (U / (D / 8) == (kk >> 2)) {
+                    const uint4 nv = *reinterpret_cast<const uint4*>(rv + 8 * (U % (D / 8)));
+                    switch (kk & 3) {
+                        case 0: vr[uu][0] = nv; break;
+                        case 1: vr[uu][1] = nv; break;
+                        case 2: vr[uu][2] = nv; break;
+                        default: vr[uu][3] = nv; break;
+                    }
+                }
             }
         }
     }
-    auto valid = [&](int cs) -> bool {
-        if (cs >= S || t < 0) return false;
-        if (cs < s) return cs <= t;
-        if (cs < s + C) return (cs - s) < new_cnt;
-        // ring slot r holds token t - d, d = (tslot - r) mod w: valid when >= max(s, 0)
-        const int r = cs - s - C;
-        const int d = (r <= tslot) ? tslot - r : tslot - r + w;
-        return int64_t(d) <= t - s;
-    };
+    // validity of the 64 slots as a wave-wide bit mask (lane k tests slot slot0 + k)
+    uint64_t vmask;
+    {
+        const int cs = slot0 + lane;
+        bool ok = false;
+        if (cs < S && t >= 0) {
+            if (cs < s) {
+                ok = cs <= t;
+            } else if (cs < s + C) {
+                ok = (cs - s) < new_cnt;
+            } else {
+                // ring slot r holds token t - d, d = (tslot - r) mod w: valid when >= s
+                const int r = cs - s - C;
+                const int d = (r <= tslot) ? tslot - r : tslot - r + w;
+                ok = d <= t - s;
+            }
+        }
+        vmask = __ballot(ok);
+    }
+    auto valid = [&](int k) -> bool { return (vmask >> k) & 1ull; };
 
     // the wave owning the slot the leaving token takes also moves its row there
     if (INGEST && X >= 0) {
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const bool ok = valid(slot0 + 16 * mt + 4 * q16 + r);
+            const bool ok = valid(16 * mt + 4 * q16 + r);
             x[mt][r] = ok ? sacc[mt][r] * csc : -INFINITY;
             m = fmaxf(m, x[mt][r]);
         }
@@ -439,29 +456,40 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 }
 
 // Merge of the split partials (fixed split order) and, for a decode step, the
-// rest of the ingest.  One workgroup per (batch, KV head).
-template <int D, bool INGEST>
+// rest of the ingest.  One workgroup per (batch, KV head).  Every load that
+// does not depend on another is issued first: the state words, k_t/v_t, the
+// segment entries (for a possible weakest-entry search), every split's
+// (max, sum) and the first CH splits' o values.
+template <int D, int G, bool INGEST>
 __global__ __launch_bounds__(256) void decode_finish_kernel(
-    int Hq, int Hkv, int G, int s, int w, int C, int S, int nsplit,
-    const uint16_t* __restrict__ k_t, const uint16_t* __restrict__ v_t, lte_cnn cnn, CacheView c,
-    const float* __restrict__ part, uint16_t* __restrict__ out_t) {
-    __shared__ __align__(16) unsigned char smem[INGEST ? ScoreSmem<D>::kBytes : 16];
-    __shared__ float fw[2 * kMaxG];
+    int Hq, int Hkv, int s, int w, int C, int S, int nsplit, const uint16_t* __restrict__ k_t,
+    const uint16_t* __restrict__ v_t, lte_cnn cnn, CacheView c, const float* __restrict__ part,
+    uint16_t* __restrict__ out_t) {
+    constexpr int NO = (G * D + 255) / 256;                  // outputs per thread
+    constexpr int CH = (64 / NO < 2) ? 2 : (64 / NO > 32 ? 32 : 64 / NO);   // splits per round
+    constexpr int kSplitMax = (kMaxSink + kMaxCapacity + 32768 + KPB - 1) / KPB;
+    constexpr int kFw = kSplitMax * G * 4;
+    constexpr int kBuf = (INGEST && ScoreSmem<D>::kBytes > kFw) ? ScoreSmem<D>::kBytes : kFw;
+    __shared__ __align__(16) unsigned char smem[kBuf];       // split weights; later the scorer
+    __shared__ float invL[G];
     __shared__ float w2s[INGEST ? kHidden * 3 : 1];
     __shared__ float red_s[4];
     __shared__ int red_t[4], red_x[4];
+    float* fw = reinterpret_cast<float*>(smem);              // [nsplit][G]
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int bg = blockIdx.x;
     const int b = bg / Hkv;
     const int g = bg % Hkv;
-    (void)smem;
+    const long stride = long(G) * (D + 2);                   // floats per split
+    const float* p0 = part + long(bg) * nsplit * stride;
 
-    // the ingest's inputs: the state before any write of this step
+    // ---- round 1 -----------------------------------------------------------------------
     int64_t t = 0, u = 0;
     int cnt = 0, X = -1, wk = -1;
-    float rl = 0.0f, ws = 0.0f;
+    float rl = 0.0f;
     if (INGEST) {
         t = c.pos[bg];
         cnt = c.count[bg];
@@ -469,57 +497,83 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(
         rl = c.nx_score[bg];
         u = c.next_unscored[bg];
         wk = c.weak[bg];
-        ws = (wk >= 0) ? c.ret_score[long(bg) * C + wk] : 0.0f;
+    }
+    float ov[NO][CH];
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+        const int x = tid + 256 * j;
+        const int hh = x / D;
+        const int dd = x % D;
+#pragma unroll
+        for (int q = 0; q < CH; ++q)
+            ov[j][q] = (x < G * D && q < nsplit) ? p0[q * stride + hh * (D + 2) + 2 + dd] : 0.0f;
+    }
+    constexpr int kMl = (kSplitMax + 63) / 64;
+    float mv[(G + 3) / 4][kMl], lv[(G + 3) / 4][kMl];
+#pragma unroll
+    for (int j = 0; j < (G + 3) / 4; ++j) {
+        const int hh = wave + 4 * j;
+#pragma unroll
+        for (int q = 0; q < kMl; ++q) {
+            const int sp = lane + 64 * q;
+            const bool ok = hh < G && sp < nsplit;
+            mv[j][q] = ok ? p0[sp * stride + hh * (D + 2)] : -INFINITY;
+            lv[j][q] = ok ? p0[sp * stride + hh * (D + 2) + 1] : 0.0f;
+        }
     }
 
-    // per head: M = max of the split maxima, 1/L with L = sum l_sp 2^(m_sp - M)
-    const float* p0 = part + long(bg) * nsplit * G * (D + 2);
-    for (int hh = wave; hh < G; hh += 4) {
-        float M = -INFINITY;
-        for (int x = lane; x < nsplit; x += 64) M = fmaxf(M, p0[(long(x) * G + hh) * (D + 2)]);
+    // ---- per head: M = max of the split maxima, weights 2^(m_sp - M), 1/L ---------------
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        float L = 0.0f;
-        for (int x = lane; x < nsplit; x += 64) {
-            const float mm = p0[(long(x) * G + hh) * (D + 2)];
-            if (mm != -INFINITY)
-                L += __builtin_amdgcn_exp2f(mm - M) * p0[(long(x) * G + hh) * (D + 2) + 1];
-        }
+    for (int j = 0; j < (G + 3) / 4; ++j) {
+        const int hh = wave + 4 * j;
+        if (hh < G) {
+            float M = -INFINITY;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-        if (lane == 0) {
-            fw[hh] = M;
-            fw[kMaxG + hh] = (L > 0.0f) ? 1.0f / L : 0.0f;
+            for (int q = 0; q < kMl; ++q) M = fmaxf(M, mv[j][q]);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+            float L = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kMl; ++q) {
+                const int sp = lane + 64 * q;
+                const float f = (mv[j][q] == -INFINITY) ? 0.0f
+                                                         : __builtin_amdgcn_exp2f(mv[j][q] - M);
+                if (sp < nsplit) fw[sp * G + hh] = f;
+                L += f * lv[j][q];
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+            if (lane == 0) invL[hh] = (L > 0.0f) ? 1.0f / L : 0.0f;
         }
     }
     __syncthreads();
-    for (int x = tid; x < G * D; x += 256) {
+
+    // ---- o = sum_sp w_sp o_sp / L in split order ------------------------------------------
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+        const int x = tid + 256 * j;
+        if (x >= G * D) break;
         const int hh = x / D;
         const int dd = x % D;
-        const float M = fw[hh];
         float o = 0.0f;
-        int sp = 0;
-        for (; sp + 4 <= nsplit; sp += 4) {
-            float mv[4], ov[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                mv[q] = p0[(long(sp + q) * G + hh) * (D + 2)];
-                ov[q] = p0[(long(sp + q) * G + hh) * (D + 2) + 2 + dd];
-            }
+        for (int q = 0; q < CH; ++q)
+            if (q < nsplit) o += fw[q * G + hh] * ov[j][q];
+        for (int c0 = CH; c0 < nsplit; c0 += CH) {
+            float nv[CH];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (mv[q] != -INFINITY) o += __builtin_amdgcn_exp2f(mv[q] - M) * ov[q];
-        }
-        for (; sp < nsplit; ++sp) {
-            const float mm = p0[(long(sp) * G + hh) * (D + 2)];
-            if (mm != -INFINITY)
-                o += __builtin_amdgcn_exp2f(mm - M) * p0[(long(sp) * G + hh) * (D + 2) + 2 + dd];
+            for (int q = 0; q < CH; ++q)
+                nv[q] = (c0 + q < nsplit) ? p0[(c0 + q) * stride + hh * (D + 2) + 2 + dd] : 0.0f;
+#pragma unroll
+            for (int q = 0; q < CH; ++q)
+                if (c0 + q < nsplit) o += fw[(c0 + q) * G + hh] * nv[q];
         }
         reinterpret_cast<__bf16*>(out_t)[(long(b) * Hq + g * G + hh) * D + dd] =
-            (__bf16)(o * fw[kMaxG + hh]);
+            (__bf16)(o * invL[hh]);
     }
     if (INGEST) {
-        __syncthreads();
+        const float ws = (wk >= 0) ? c.ret_score[long(bg) * C + wk] : 0.0f;
+        __syncthreads();                              // split weights no longer read
         ingest_finish<D>(c, bg, g, s, w, C, S, t, cnt, X, rl, u, wk, ws, false, k_t, v_t, cnn,
                          smem, w2s, red_s, red_t, red_x);
     }
@@ -548,21 +602,33 @@ hipError_t launch_decode(const Shape& sh, bool ingest, const uint16_t* q_t, cons
     dim3 fgrid(unsigned(sh.B * sh.Hkv));
     lte_cnn cn{};
     if (cnn != nullptr) cn = *cnn;
+#define LTE_FINISH(DD, GG, ING)                                                                  \
+    case GG:                                                                                     \
+        hipLaunchKernelGGL((decode_finish_kernel<DD, GG, ING>), fgrid, dim3(256), 0, st, sh.Hq, \
+                           sh.Hkv, sh.s, sh.w, sh.C, sh.S, nsplit, k_t, v_t, cn, cache, part,    \
+                           out_t);                                                               \
+        break;
 #define LTE_DECODE(DD, ING)                                                                      \
     do {                                                                                         \
         hipLaunchKernelGGL((decode_split_kernel<DD, ING>), grid, dim3(64), 0, st, sh.Hq, sh.Hkv, \
                            sh.G, sh.s, sh.w, sh.C, sh.S, nsplit, q_t, k_t, v_t, cache, part);    \
         hipError_t e_ = hipGetLastError();                                                       \
         if (e_ != hipSuccess) return e_;                                                         \
-        hipLaunchKernelGGL((decode_finish_kernel<DD, ING>), fgrid, dim3(256), 0, st, sh.Hq,     \
-                           sh.Hkv, sh.G, sh.s, sh.w, sh.C, sh.S, nsplit, k_t, v_t, cn, cache,    \
-                           part, out_t);                                                         \
+        switch (sh.G) {                                                                          \
+            LTE_FINISH(DD, 1, ING)                                                               \
+            LTE_FINISH(DD, 2, ING)                                                               \
+            LTE_FINISH(DD, 4, ING)                                                               \
+            LTE_FINISH(DD, 8, ING)                                                               \
+            LTE_FINISH(DD, 16, ING)                                                              \
+            default: return hipErrorInvalidValue;                                                \
+        }                                                                                        \
     } while (0)
     if (sh.D == 128) {
         if (ingest) LTE_DECODE(128, true); else LTE_DECODE(128, false);
     } else {
         if (ingest) LTE_DECODE(64, true); else LTE_DECODE(64, false);
     }
+#undef LTE_FINISH
 #undef LTE_DECODE
     return hipGetLastError();
 }
