@@ -18,9 +18,16 @@
 //     A lane then owns one query row, so the row max/sum of the online
 //     softmax is a 32-value local reduction plus one lane swap.
 //   * O^T += V^T P^T: P^T comes straight from the S^T accumulator (converted
-//     to bf16); V is stored transposed in LDS with the key order permuted to
-//     match the accumulator's row order, so no data moves between lanes.
-//   * fp32 softmax with exp2 and max subtraction; masked keys are -inf.
+//     to bf16).  V stays row-major in LDS; its MFMA operand (8 keys of one
+//     dim per lane) is read with ds_read_b64_tr_b16, whose 16-lane transpose
+//     turns four 4-dim row pieces into four keys of one dim per lane.
+//   * K and V tiles sit in LDS as 16-byte chunks XOR-swizzled by row, so the
+//     row-strided MFMA operand reads hit distinct banks.
+//   * the next block's K/V rows are fetched into registers while the current
+//     block computes, then written to LDS between two barriers.
+//   * fp32 online softmax on raw logits, the 1/sqrt(D) scale and log2(e)
+//     folded into one FMA before exp2; masked keys are -inf; the running
+//     output is rescaled only when some row's maximum moved.
 #include "lte_internal.h"
 
 namespace lte {
@@ -30,8 +37,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS chunk swizzle of tile row r (a key): bits (r&3)<<1 | (r>>2)&1, a
+// permutation of 0..7 over any 8 consecutive rows starting at a multiple of 8.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void attend_prefill_kernel(
+__global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
     int T, int Hq, int Hkv, int s, int w, int ntile, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ thr,
@@ -39,17 +50,17 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     constexpr int P = 128 / G;          // positions per tile
     constexpr int KK = D / 16;          // MFMA k-steps of q.k
     constexpr int DT = D / 32;          // 32-wide output tiles of o
-    constexpr int KST = D + 8;          // LDS row stride of K (bf16)
-    constexpr int VST = 64 + 8;         // LDS row stride of V^T (bf16)
+    constexpr int CPR = D / 8;          // 16-byte chunks per key row
+    constexpr int NCH = 64 * CPR / 256; // chunks of one 64-key tile per thread
     constexpr int kMaxList = kMaxSink + kMaxCapacity;
-    constexpr int DV = D / 8;           // 16-byte chunks per key row
 
-    __shared__ __align__(16) __bf16 Ks[64 * KST];
-    __shared__ __align__(16) __bf16 Vt[D * VST];
-    __shared__ __align__(16) uint32_t lst[kMaxList];   // (rank << 16) | token index
-    __shared__ __align__(16) int32_t brank[64];
+    __shared__ __align__(16) u32x4 Ks[64 * CPR];          // swizzled row-major K tile
+    __shared__ __align__(16) u32x4 Vs[64 * CPR];          // swizzled row-major V tile
+    // (field << 16) | token index; field = rank + 1 of a retained token, 0 for
+    // a sink token, 0xffff for padding
+    __shared__ __align__(16) uint32_t lst[kMaxList];
+    __shared__ __align__(16) int32_t brank[128];
     __shared__ int wsum[4];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -58,9 +69,9 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so map
     // each XCD's share to a contiguous run of tiles (neighbouring tiles of a
     // head share most of their band keys in that XCD's L2).
-    const int nblk = gridDim.x;
+    const int ngrid = gridDim.x;
     int lin = blockIdx.x;
-    if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    if ((ngrid & 7) == 0) lin = (blockIdx.x & 7) * (ngrid >> 3) + (blockIdx.x >> 3);
     const int bg = lin / ntile;
     const int tile = lin % ntile;
     const int b = bg / Hkv;
@@ -81,19 +92,17 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     if (band_lo > 0) {
         const int thr0 = th[i0 - w];
         ns = min(s, band_lo);
-        for (int j = tid; j < ns; j += 256) lst[j] = uint32_t(j);
+        for (int j = tid; j < ns; j += 256) lst[j] = uint32_t(j);     // field 0: always visible
         len = ns;
         // candidates j in [s, band_lo) alive at the first row, in index order
         for (int base = s; base < band_lo; base += 256 * 16) {
-            uint32_t ent[16];
-            int cnt = 0;
             const int j0 = base + tid * 16;
             int rr[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) rr[u] = (j0 + u < band_lo) ? rk[j0 + u] : kNotCand;
+            int cnt = 0;
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                if (rr[u] <= thr0) ent[cnt++] = (uint32_t(rr[u]) << 16) | uint32_t(j0 + u);
+                rr[u] = (j0 + u < band_lo) ? rk[j0 + u] : kNotCand;
+                cnt += (rr[u] <= thr0) ? 1 : 0;
             }
             // block exclusive scan of cnt
             int incl = cnt;
@@ -110,14 +119,16 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
                 woff += (x < wave) ? wsum[x] : 0;
                 tot += wsum[x];
             }
-            const int off = len + woff + incl - cnt;
+            int o = len + woff + incl - cnt;
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                if (u < cnt) lst[off + u] = ent[u];
+                if (rr[u] <= thr0) lst[o++] = (uint32_t(rr[u] + 1) << 16) | uint32_t(j0 + u);
             }
             len += tot;
             __syncthreads();
         }
+        // pad to whole blocks with entries no row sees (field 0xffff, key 0)
+        for (int e = len + tid; e < ((len + 63) & ~63); e += 256) lst[e] = 0xffff0000u;
     }
     __syncthreads();
 
@@ -137,6 +148,8 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
             qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + half * 8);
     }
     const int thr_row = (irow - w >= 0) ? th[irow - w] : -2;
+    // list entry e is visible to this row iff e <= lim (field <= thr_row + 1)
+    const uint32_t lim = (uint32_t(min(max(thr_row + 1, 0), 0xfffe)) << 16) | 0xffffu;
     const float csc = kLog2e * rsqrtf(float(D));
 
     float m_run = -INFINITY;
@@ -148,63 +161,57 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     const int nlist = (len + 63) / 64;
     const int nband = (band_hi - band_lo + 1 + 63) / 64;
 
-    for (int blk = 0; blk < nlist + nband; ++blk) {
+    // ranks of the first 128 band keys: a band key j can be a retained column
+    // of a row of the tile only if j <= i_last - w < band_lo + P - 1 <= band_lo + 127
+    if (tid < 128) {
+        const int j = band_lo + tid;
+        brank[tid] = (j < s) ? -1 : ((j <= band_hi) ? rk[j] : kNotCand);   // sink always passes
+    }
+
+    // Chunk c = tid + 256x of a 64-key tile is stored chunk c % CPR of tile row
+    // c / CPR and holds that key's 8-dim chunk (c % CPR) ^ swz(row).  swz puts
+    // 8 consecutive rows on 8 distinct bank groups (row-strided K reads) and
+    // the 4-row x 2-chunk patch of one 16-lane transposing V read likewise.
+    // The list entry is read for band blocks too (clamped, unused) so that the
+    // fetch stays branch-free.
+    int frow[NCH], fchk[NCH];
+#pragma unroll
+    for (int x = 0; x < NCH; ++x) {
+        const int c = tid + 256 * x;
+        frow[x] = c / CPR;
+        fchk[x] = ((c % CPR) ^ swz(frow[x])) * 8;
+    }
+    const int nblk = nlist + nband;
+    u32x4 kpre[NCH], vpre[NCH];
+#define LTE_FETCH(BLK)                                                                   \
+    {                                                                                    \
+        const int fb = (BLK);                                                            \
+        _Pragma("unroll") for (int x = 0; x < NCH; ++x) {                                \
+            const int e = fb * 64 + frow[x];                                             \
+            const int lrow = int(lst[min(e, kMaxList - 1)] & 0xffffu);                   \
+            const int brow = min(band_lo + (fb - nlist) * 64 + frow[x], band_hi);        \
+            const int row = (fb < nlist) ? lrow : brow;                                  \
+            const long off = long(row) * kv_row + fchk[x];                               \
+            kpre[x] = *reinterpret_cast<const u32x4*>(kbase + off);                        \
+            vpre[x] = *reinterpret_cast<const u32x4*>(vbase + off);                        \
+        }                                                                                \
+    }
+#define LTE_STAGE()                                                                      \
+    {                                                                                    \
+        _Pragma("unroll") for (int x = 0; x < NCH; ++x) {                                \
+            Ks[tid + 256 * x] = kpre[x];                                                 \
+            Vs[tid + 256 * x] = vpre[x];                                                 \
+        }                                                                                \
+    }
+    LTE_FETCH(0)
+    __syncthreads();                              // band ranks visible
+    LTE_STAGE()
+    __syncthreads();
+
+    for (int blk = 0; blk < nblk; ++blk) {
         const bool is_list = blk < nlist;
         const int jb0 = band_lo + (blk - nlist) * 64;     // first key of a band block
-
-        // ---- stage K (row-major) and V^T (permuted key order) into LDS ---------
-#pragma unroll
-        for (int x = 0; x < (64 * DV) / 256; ++x) {
-            const int c16 = tid + 256 * x;
-            const int t = c16 / DV;
-            const int col = c16 % DV;
-            int j;
-            if (is_list) {
-                const int e = blk * 64 + t;
-                j = (e < len) ? int(lst[e] & 0xffffu) : 0;
-            } else {
-                j = min(jb0 + t, band_hi);
-            }
-            *reinterpret_cast<uint4*>(&Ks[t * KST + col * 8]) =
-                *reinterpret_cast<const uint4*>(kbase + long(j) * kv_row + col * 8);
-        }
-        if (tid < 16 * DV) {
-            const int kg = tid / DV;          // 4 consecutive keys 4kg .. 4kg+3
-            const int dg = tid % DV;          // 8 consecutive dims 8dg .. 8dg+7
-            uint4 rows[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int t = 4 * kg + u;
-                int j;
-                if (is_list) {
-                    const int e = blk * 64 + t;
-                    j = (e < len) ? int(lst[e] & 0xffffu) : 0;
-                } else {
-                    j = min(jb0 + t, band_hi);
-                }
-                rows[u] = *reinterpret_cast<const uint4*>(vbase + long(j) * kv_row + dg * 8);
-            }
-            // keys 4q..4q+3 of each 16-key chunk go to positions (q&1)*8 + (q>>1)*4,
-            // so lane half 0 reads keys {0-3, 8-11} and half 1 keys {4-7, 12-15}
-            const int qq = kg & 3;
-            const int pos = (kg >> 2) * 16 + (qq & 1) * 8 + (qq >> 1) * 4;
-            const uint16_t* r0 = reinterpret_cast<const uint16_t*>(&rows[0]);
-            const uint16_t* r1 = reinterpret_cast<const uint16_t*>(&rows[1]);
-            const uint16_t* r2 = reinterpret_cast<const uint16_t*>(&rows[2]);
-            const uint16_t* r3 = reinterpret_cast<const uint16_t*>(&rows[3]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint2 pk;
-                pk.x = uint32_t(r0[e]) | (uint32_t(r1[e]) << 16);
-                pk.y = uint32_t(r2[e]) | (uint32_t(r3[e]) << 16);
-                *reinterpret_cast<uint2*>(&Vt[(dg * 8 + e) * VST + pos]) = pk;
-            }
-        }
-        if (!is_list && tid < 64) {
-            const int j = jb0 + tid;
-            brank[tid] = (j <= band_hi) ? rk[j] : kNotCand;
-        }
-        __syncthreads();
+        if (blk + 1 < nblk) LTE_FETCH(blk + 1)            // in flight during this block
 
         // ---- S^T = K Q^T for 64 keys x this wave's 32 rows -----------------------
         f32x16 sacc[2];
@@ -214,14 +221,13 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
         for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &Ks[(ks * 32 + (lane & 31)) * KST + kk * 16 + half * 8]);
+                const int row = ks * 32 + (lane & 31);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, Ks[row * CPR + ((2 * kk + half) ^ swz(row))]);
                 sacc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[ks], 0, 0, 0);
             }
         }
-
-        // ---- mask and scale: element e of subtile ks is key slot
-        //      ks*32 + (e/4)*8 + half*4 + e%4 of this block ---------------------------
+        // ---- mask: element e of subtile ks is key slot
+        //      ks*32 + (e/4)*8 + half*4 + e%4 of this block ----------------------------
         float x[2][16];
         if (is_list) {
 #pragma unroll
@@ -229,14 +235,10 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int t0 = ks * 32 + e4 * 8 + half * 4;
-                    const uint4 ent = *reinterpret_cast<const uint4*>(&lst[blk * 64 + t0]);
-                    const uint32_t ev[4] = {ent.x, ent.y, ent.z, ent.w};
+                    const u32x4 ent = *reinterpret_cast<const u32x4*>(&lst[blk * 64 + t0]);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int eidx = blk * 64 + t0 + u;
-                        const bool vis = (eidx < ns) || (eidx < len && int(ev[u] >> 16) <= thr_row);
-                        x[ks][e4 * 4 + u] = vis ? sacc[ks][e4 * 4 + u] * csc : -INFINITY;
-                    }
+                    for (int u = 0; u < 4; ++u)
+                        x[ks][e4 * 4 + u] = (ent[u] <= lim) ? sacc[ks][e4 * 4 + u] : -INFINITY;
                 }
             }
         } else {
@@ -245,29 +247,33 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) x[ks][e] = sacc[ks][e] * csc;
+                    for (int e = 0; e < 16; ++e) x[ks][e] = sacc[ks][e];
             } else {
+                // d = irow - j: visible iff 0 <= d < w, or d >= w and j passes
+                // (sink ranks read -1); blocks past the second hold no d >= w
+                const int rb = min(blk - nlist, 1) * 64;
+                const int dbase = irow - jb0 - half * 4;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                     for (int e4 = 0; e4 < 4; ++e4) {
                         const int t0 = ks * 32 + e4 * 8 + half * 4;
-                        const int4 br = *reinterpret_cast<const int4*>(&brank[t0]);
+                        const int4 br = *reinterpret_cast<const int4*>(&brank[rb + t0]);
                         const int bv[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const int j = jb0 + t0 + u;
-                            const bool vis =
-                                (j <= irow) &&
-                                (j >= irow - w + 1 || j < s || (j <= irow - w && bv[u] <= thr_row));
-                            x[ks][e4 * 4 + u] = vis ? sacc[ks][e4 * 4 + u] * csc : -INFINITY;
+                            const int d = dbase - (ks * 32 + e4 * 8 + u);
+                            const bool vis = (unsigned(d) < unsigned(w)) |
+                                             ((d >= 0) & (bv[u] <= thr_row));
+                            x[ks][e4 * 4 + u] = vis ? sacc[ks][e4 * 4 + u] : -INFINITY;
                         }
                     }
                 }
             }
         }
 
-        // ---- online softmax (row = this lane's query; keys split with lane^32) -----
+        // ---- online softmax in raw logits (scale folded into the exponent; row =
+        //      this lane's query, keys split with lane^32) ------------------------------
         float mloc = x[0][0];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -276,35 +282,63 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
         const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
         const float m_new = fmaxf(m_run, mrow);
         const float msafe = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - msafe);
+        const float alpha = fast_exp2((m_run - msafe) * csc);
+        const float moff = -msafe * csc;
         float lsum = 0.0f;
         bf16x8 pf[4];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = fast_exp2(x[ks][e] - msafe);
+                const float p = fast_exp2(fmaf(x[ks][e], csc, moff));
                 lsum += p;
                 pf[ks * 2 + (e >> 3)][e & 7] = (__bf16)p;
             }
         }
         l_run = l_run * alpha + lsum;
         m_run = m_new;
+        if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+            for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+        }
 
         // ---- O^T += V^T P^T ------------------------------------------------------
+        // operand element e of lane (16-group G, index i) is V[key][dt*32 + (G&1)*16 + i]
+        // with key = cc*16 + (e<4 ? 4h + e : 8 + 4h + e-4), h = lane/32: two
+        // transposing reads, each of 4 keys, from rows that lane i of the group names
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &Vt[(dt * 32 + (lane & 31)) * VST + cc * 16 + half * 8]);
+                bf16x8 a;
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int grp = lane >> 4;
+                    const int i = lane & 15;
+                    const int key = cc * 16 + 8 * r + 4 * (grp >> 1) + (i >> 2);
+                    const int d0 = dt * 32 + (grp & 1) * 16 + 4 * (i & 3);
+                    const int chunk = (d0 >> 3) ^ swz(key);
+                    const __bf16* src = reinterpret_cast<const __bf16*>(&Vs[key * CPR + chunk]) + (d0 & 7);
+                    typedef short v4i16 __attribute__((ext_vector_type(4)));
+                    const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16*)(src));
+                    const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
+                    a[4 * r + 0] = b4[0];
+                    a[4 * r + 1] = b4[1];
+                    a[4 * r + 2] = b4[2];
+                    a[4 * r + 3] = b4[3];
+                }
                 acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[cc], acc_o[dt], 0, 0, 0);
             }
         }
-        __syncthreads();
+        __syncthreads();                          // every wave is done with the tiles
+        if (blk + 1 < nblk) {
+            LTE_STAGE()
+            __syncthreads();
+        }
     }
+#undef LTE_FETCH
+#undef LTE_STAGE
 
     // ---- normalise and store: element e of d-tile dt is dim dt*32 + (e/4)*8 + half*4 + e%4
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
