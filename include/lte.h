@@ -39,8 +39,9 @@
  *     LTE_ERR_HIP.  No C++ exception crosses this interface.
  *   - Sequences of a batch have equal length.
  *   - Supported: head_dim in {64, 128}; q_heads / kv_heads in {1, 2, 4, 8,
- *     16}; hidden == 32; 5 <= window <= 32768; 0 <= sink <= 256;
- *     0 <= capacity <= 4096; 1 <= T <= 32768 tokens per prefill.
+ *     16}; kv_heads <= 128; hidden == 32; 5 <= window <= 32768;
+ *     0 <= sink <= 256; 0 <= capacity <= 4096; 1 <= T <= 32768 tokens per
+ *     prefill.
  */
 #ifndef LTE_H
 #define LTE_H

@@ -22,6 +22,9 @@ int check_cfg(const lte_config* cfg) {
     if (c.hidden != kHidden) return LTE_ERR_UNSUPPORTED;
     if (c.window < 5 || c.window > 32768) return LTE_ERR_UNSUPPORTED;
     if (c.sink > kMaxSink || c.capacity > kMaxCapacity) return LTE_ERR_UNSUPPORTED;
+    // one sequence's K or V rows span T * kv_heads * head_dim * 2 bytes, addressed
+    // with 32-bit offsets: kv_heads <= 128 keeps that below 2^31 at T = 32768
+    if (c.kv_heads > 128) return LTE_ERR_UNSUPPORTED;
     if (long(c.batch) * c.kv_heads > (1L << 20)) return LTE_ERR_UNSUPPORTED;
     return LTE_OK;
 }

@@ -6,13 +6,17 @@
 // Query row i sees V(i) = [0, min(s, i+1)) U [i-w+1, i] U R_i, with
 // j in R_i <=> j <= i-w and rank[j] <= thr[i-w] (selection kernel).
 //
-// Tiling (one workgroup = 4 waves = 128 MFMA rows):
+// Tiling (one workgroup = 8 waves = 256 MFMA rows, one workgroup per CU):
 //   * GQA packing: the G = Hq/Hkv query heads of a group share their keys, so
-//     a tile is P = 128/G consecutive positions x G heads of one KV head.
+//     a tile is P = 256/G consecutive positions x G heads of one KV head.
 //     Its band of keys is [i0-w+1, i0+P-1] (P+w-1 keys for P rows).
-//   * keys are processed in blocks of 64: first the gathered columns below the
-//     band (sink + retained tokens alive at the tile's first row, via the
-//     per-head rank/thr lists), then the band blocks.
+//   * keys are processed in blocks of 64: first the band blocks, then the
+//     gathered columns below the band (sink + retained tokens alive at the
+//     tile's first row, via the per-head rank/thr lists), which are listed
+//     while the first band block loads.
+//   * K/V tiles are double-buffered in LDS and filled by direct global->LDS
+//     loads issued one block ahead, so one barrier per block suffices; the
+//     two waves sharing a SIMD then alternate between MFMA and softmax work.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows from LDS are the A
 //     operand, each wave's 32 query rows stay in registers as the B operand.
 //     A lane then owns one query row, so the row max/sum of the online
@@ -23,11 +27,10 @@
 //     turns four 4-dim row pieces into four keys of one dim per lane.
 //   * K and V tiles sit in LDS as 16-byte chunks XOR-swizzled by row, so the
 //     row-strided MFMA operand reads hit distinct banks.
-//   * the next block's K/V rows are fetched into registers while the current
-//     block computes, then written to LDS between two barriers.
 //   * fp32 online softmax on raw logits, the 1/sqrt(D) scale and log2(e)
-//     folded into one FMA before exp2; masked keys are -inf; the running
-//     output is rescaled only when some row's maximum moved.
+//     folded into one FMA before exp2; masked keys are -inf; the reference
+//     maximum of a row moves only when exceeded by more than 2^8 in the
+//     exponent, so the running output is rarely rescaled.
 #include "lte_internal.h"
 
 namespace lte {
@@ -37,30 +40,49 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS chunk swizzle of tile row r (a key): bits (r&3)<<1 | (r>>2)&1, a
-// permutation of 0..7 over any 8 consecutive rows starting at a multiple of 8.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS chunk swizzle of tile row r (a key): the 16-byte chunk c of row r is
+// stored at chunk position c ^ swz(r).  Two access patterns must spread over
+// the banks: the K operand reads one chunk of 8 (or 16) consecutive rows, the
+// transposing V read two (or four) adjacent chunks of 4 consecutive rows.
+// D = 128 (256-byte rows): swz(r) = T[r & 3] ^ ((r >> 2) & 3) with
+// T = {0, 10, 4, 14}, which maps any aligned 8 rows to distinct positions mod
+// 8 and 16 rows to distinct positions mod 16, and (row, chunk) of both V
+// patterns likewise.  D = 64 (128-byte rows): 3 bits, (r&3)<<1 | (r>>2)&1.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return (((r & 1) * 10) | ((r & 2) << 1)) ^ ((r >> 2) & 3);
+    else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
 
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
+__global__ __launch_bounds__(512) void attend_prefill_kernel(
     int T, int Hq, int Hkv, int s, int w, int ntile, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ thr,
     uint16_t* __restrict__ out) {
-    constexpr int P = 128 / G;          // positions per tile
-    constexpr int KK = D / 16;          // MFMA k-steps of q.k
-    constexpr int DT = D / 32;          // 32-wide output tiles of o
-    constexpr int CPR = D / 8;          // 16-byte chunks per key row
-    constexpr int NCH = 64 * CPR / 256; // chunks of one 64-key tile per thread
+    constexpr int NW = 8;                   // waves
+    constexpr int P = NW * 32 / G;          // positions per tile
+    constexpr int KK = D / 16;              // MFMA k-steps of q.k
+    constexpr int DT = D / 32;              // 32-wide output tiles of o
+    constexpr int CPR = D / 8;              // 16-byte chunks per key row
+    constexpr int TCH = 64 * CPR;           // chunks of one 64-key tile
+    constexpr int LPW = TCH / 64 / NW;      // direct loads per wave per tile and tensor
     constexpr int kMaxList = kMaxSink + kMaxCapacity;
+    constexpr int kBr = P > 64 ? P : 64;    // band keys whose rank can matter, rounded up
+    static_assert(LPW >= 1 && LPW * 64 * NW == TCH, "tile split");
 
-    __shared__ __align__(16) u32x4 Ks[64 * CPR];          // swizzled row-major K tile
-    __shared__ __align__(16) u32x4 Vs[64 * CPR];          // swizzled row-major V tile
+    // double-buffered swizzled K and V tiles, one object per buffer so that the
+    // compiler can tell a tile being read from the one being loaded
+    __shared__ __align__(16) u32x4 K0[TCH];
+    __shared__ __align__(16) u32x4 V0[TCH];
+    __shared__ __align__(16) u32x4 K1[TCH];
+    __shared__ __align__(16) u32x4 V1[TCH];
     // (field << 16) | token index; field = rank + 1 of a retained token, 0 for
     // a sink token, 0xffff for padding
     __shared__ __align__(16) uint32_t lst[kMaxList];
-    __shared__ __align__(16) int32_t brank[128];
-    __shared__ int wsum[4];
+    __shared__ __align__(16) int32_t brank[kBr];
+    __shared__ int lfull[kMaxList / 64];            // list block visible to every row of the tile
+    __shared__ int wsum[NW];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -80,57 +102,48 @@ __global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
     const int i_last = min(i0 + P, T) - 1;
     const int band_lo = max(0, i0 - w + 1);
     const int band_hi = i_last;
+    const int nband = (band_hi - band_lo + 1 + 63) / 64;
     const int32_t* rk = rank + long(bg) * T;
     const int32_t* th = thr + long(bg) * T;
-    const long kv_row = long(Hkv) * D;                           // elements between tokens
-    const uint16_t* kbase = k + (long(b) * T * Hkv + g) * D;
-    const uint16_t* vbase = v + (long(b) * T * Hkv + g) * D;
+    // key rows of this (batch, KV head): byte offsets fit 32 bits (T * Hkv * D
+    // * 2 < 2^31 is checked on the host) and row * kv_bytes fits 24-bit factors
+    const char* kbytes = reinterpret_cast<const char*>(k + (long(b) * T * Hkv + g) * D);
+    const char* vbytes = reinterpret_cast<const char*>(v + (long(b) * T * Hkv + g) * D);
+    const uint32_t kv_bytes = uint32_t(Hkv * D * 2);
 
-    // ---- gathered columns below the band: sink, then retained tokens ----------
-    int len = 0;
-    int ns = 0;                                   // leading sink entries: always visible
-    if (band_lo > 0) {
-        const int thr0 = th[i0 - w];
-        ns = min(s, band_lo);
-        for (int j = tid; j < ns; j += 256) lst[j] = uint32_t(j);     // field 0: always visible
-        len = ns;
-        // candidates j in [s, band_lo) alive at the first row, in index order
-        for (int base = s; base < band_lo; base += 256 * 16) {
-            const int j0 = base + tid * 16;
-            int rr[16];
-            int cnt = 0;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                rr[u] = (j0 + u < band_lo) ? rk[j0 + u] : kNotCand;
-                cnt += (rr[u] <= thr0) ? 1 : 0;
-            }
-            // block exclusive scan of cnt
-            int incl = cnt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                int y = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += y;
-            }
-            if (lane == 63) wsum[wave] = incl;
-            __syncthreads();
-            int woff = 0, tot = 0;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                woff += (x < wave) ? wsum[x] : 0;
-                tot += wsum[x];
-            }
-            int o = len + woff + incl - cnt;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                if (rr[u] <= thr0) lst[o++] = (uint32_t(rr[u] + 1) << 16) | uint32_t(j0 + u);
-            }
-            len += tot;
-            __syncthreads();
-        }
-        // pad to whole blocks with entries no row sees (field 0xffff, key 0)
-        for (int e = len + tid; e < ((len + 63) & ~63); e += 256) lst[e] = 0xffff0000u;
+    // Blocks: the band blocks first, then the gathered columns below the band.
+    // A tile is filled by direct global->LDS loads: load x of wave wv writes
+    // tile chunks [64x', 64x'+64), x' = wv*LPW + x, lane l chunk 64x'+l; chunk
+    // c is stored chunk c % CPR of tile row c / CPR and holds that key's chunk
+    // (c % CPR) ^ swz(row).
+#define LTE_ISSUE(BLK, KB, VB)                                                              \
+    {                                                                                      \
+        const int fb = (BLK);                                                              \
+        _Pragma("unroll") for (int x = 0; x < LPW; ++x) {                                  \
+            const int xi = wave * LPW + x;                                                 \
+            const int c = xi * 64 + lane;                                                  \
+            const int trow = c / CPR;                                                      \
+            const int gch = (c % CPR) ^ swz<D>(trow);                                      \
+            int row;                                                                       \
+            if (fb < nband) row = min(band_lo + fb * 64 + trow, band_hi);                  \
+            else row = int(lst[min((fb - nband) * 64 + trow, kMaxList - 1)] & 0xffffu);    \
+            const uint32_t off = __umul24(uint32_t(row), kv_bytes) + uint32_t(gch * 16);   \
+            __builtin_amdgcn_global_load_lds(                                              \
+                (const __attribute__((address_space(1))) void*)(kbytes + off),             \
+                (__attribute__((address_space(3))) void*)(&KB[xi * 64]), 16, 0, 0);         \
+            __builtin_amdgcn_global_load_lds(                                              \
+                (const __attribute__((address_space(1))) void*)(vbytes + off),             \
+                (__attribute__((address_space(3))) void*)(&VB[xi * 64]), 16, 0, 0);         \
+        }                                                                                  \
     }
-    __syncthreads();
+    LTE_ISSUE(0, K0, V0)                          // first band block: needs no list
+
+    // ranks of the first kBr band keys: a band key j can be a retained column
+    // of a row of the tile only if j <= i_last - w <= band_lo + P - 2
+    for (int t = tid; t < kBr; t += NW * 64) {
+        const int j = band_lo + t;
+        brank[t] = (j < s) ? -1 : ((j <= band_hi) ? rk[j] : kNotCand);   // sink always passes
+    }
 
     // ---- this lane's query row --------------------------------------------------
     const int rtile = wave * 32 + (lane & 31);
@@ -152,66 +165,79 @@ __global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
     const uint32_t lim = (uint32_t(min(max(thr_row + 1, 0), 0xfffe)) << 16) | 0xffffu;
     const float csc = kLog2e * rsqrtf(float(D));
 
+    // ---- gathered columns below the band: sink, then retained tokens ----------
+    int len = 0;
+    if (band_lo > 0) {
+        const int thr0 = th[i0 - w];
+        const int ns = min(s, band_lo);
+        for (int j = tid; j < ns; j += NW * 64) lst[j] = uint32_t(j);     // field 0: always visible
+        len = ns;
+        // candidates j in [s, band_lo) alive at the first row, in index order
+        for (int base = s; base < band_lo; base += NW * 64 * 16) {
+            const int j0 = base + tid * 16;
+            int rr[16];
+            int cnt = 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                rr[u] = (j0 + u < band_lo) ? rk[j0 + u] : kNotCand;
+                cnt += (rr[u] <= thr0) ? 1 : 0;
+            }
+            // block exclusive scan of cnt
+            int incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                int y = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += y;
+            }
+            if (lane == 63) wsum[wave] = incl;
+            __syncthreads();
+            int woff = 0, tot = 0;
+#pragma unroll
+            for (int x = 0; x < NW; ++x) {
+                woff += (x < wave) ? wsum[x] : 0;
+                tot += wsum[x];
+            }
+            int o = len + woff + incl - cnt;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (rr[u] <= thr0) lst[o++] = (uint32_t(rr[u] + 1) << 16) | uint32_t(j0 + u);
+            }
+            len += tot;
+            __syncthreads();
+        }
+        // pad to whole blocks with entries no row sees (field 0xffff, key 0)
+        for (int e = len + tid; e < ((len + 63) & ~63); e += NW * 64) lst[e] = 0xffff0000u;
+    }
+    const int nlist = (len + 63) / 64;
+    const int nblk = nband + nlist;
+    __syncthreads();                              // list complete
+    // thr is non-increasing, so the tile's last row has the strictest list
+    // threshold: a block whose entries all pass it needs no mask
+    if (nlist > 0) {
+        const int thr_last = th[i_last - w];
+        const uint32_t lim_last = (uint32_t(min(max(thr_last + 1, 0), 0xfffe)) << 16) | 0xffffu;
+        for (int bl = wave; bl < nlist; bl += NW) {
+            const bool ok = lst[bl * 64 + lane] <= lim_last;
+            const bool all = __ballot(ok) == ~0ull;
+            if (lane == 0) lfull[bl] = all ? 1 : 0;
+        }
+    }
+
     float m_run = -INFINITY;
     float l_run = 0.0f;
     f32x16 acc_o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x16{};
 
-    const int nlist = (len + 63) / 64;
-    const int nband = (band_hi - band_lo + 1 + 63) / 64;
+    __builtin_amdgcn_s_waitcnt(0);                // this wave's loads of block 0 landed
+    __syncthreads();                              // everyone's, and lfull, brank
 
-    // ranks of the first 128 band keys: a band key j can be a retained column
-    // of a row of the tile only if j <= i_last - w < band_lo + P - 1 <= band_lo + 127
-    if (tid < 128) {
-        const int j = band_lo + tid;
-        brank[tid] = (j < s) ? -1 : ((j <= band_hi) ? rk[j] : kNotCand);   // sink always passes
-    }
-
-    // Chunk c = tid + 256x of a 64-key tile is stored chunk c % CPR of tile row
-    // c / CPR and holds that key's 8-dim chunk (c % CPR) ^ swz(row).  swz puts
-    // 8 consecutive rows on 8 distinct bank groups (row-strided K reads) and
-    // the 4-row x 2-chunk patch of one 16-lane transposing V read likewise.
-    // The list entry is read for band blocks too (clamped, unused) so that the
-    // fetch stays branch-free.
-    int frow[NCH], fchk[NCH];
-#pragma unroll
-    for (int x = 0; x < NCH; ++x) {
-        const int c = tid + 256 * x;
-        frow[x] = c / CPR;
-        fchk[x] = ((c % CPR) ^ swz(frow[x])) * 8;
-    }
-    const int nblk = nlist + nband;
-    u32x4 kpre[NCH], vpre[NCH];
-#define LTE_FETCH(BLK)                                                                   \
-    {                                                                                    \
-        const int fb = (BLK);                                                            \
-        _Pragma("unroll") for (int x = 0; x < NCH; ++x) {                                \
-            const int e = fb * 64 + frow[x];                                             \
-            const int lrow = int(lst[min(e, kMaxList - 1)] & 0xffffu);                   \
-            const int brow = min(band_lo + (fb - nlist) * 64 + frow[x], band_hi);        \
-            const int row = (fb < nlist) ? lrow : brow;                                  \
-            const long off = long(row) * kv_row + fchk[x];                               \
-            kpre[x] = *reinterpret_cast<const u32x4*>(kbase + off);                        \
-            vpre[x] = *reinterpret_cast<const u32x4*>(vbase + off);                        \
-        }                                                                                \
-    }
-#define LTE_STAGE()                                                                      \
-    {                                                                                    \
-        _Pragma("unroll") for (int x = 0; x < NCH; ++x) {                                \
-            Ks[tid + 256 * x] = kpre[x];                                                 \
-            Vs[tid + 256 * x] = vpre[x];                                                 \
-        }                                                                                \
-    }
-    LTE_FETCH(0)
-    __syncthreads();                              // band ranks visible
-    LTE_STAGE()
-    __syncthreads();
-
-    for (int blk = 0; blk < nblk; ++blk) {
-        const bool is_list = blk < nlist;
-        const int jb0 = band_lo + (blk - nlist) * 64;     // first key of a band block
-        if (blk + 1 < nblk) LTE_FETCH(blk + 1)            // in flight during this block
+    // one block: issue the next block's loads into (KN, VN), compute on (KC, VC)
+    auto step = [&](const int blk, u32x4* KC, u32x4* VC, u32x4* KN, u32x4* VN) {
+        if (blk + 1 < nblk) LTE_ISSUE(blk + 1, KN, VN)     // in flight during this block
+        const bool is_list = blk >= nband;
+        const int lb = blk - nband;                        // list block index
+        const int jb0 = band_lo + blk * 64;                // first key of a band block
 
         // ---- S^T = K Q^T for 64 keys x this wave's 32 rows -----------------------
         f32x16 sacc[2];
@@ -222,37 +248,59 @@ __global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int row = ks * 32 + (lane & 31);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, Ks[row * CPR + ((2 * kk + half) ^ swz(row))]);
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, KC[row * CPR + ((2 * kk + half) ^ swz<D>(row))]);
                 sacc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[ks], 0, 0, 0);
             }
         }
-        // ---- mask: element e of subtile ks is key slot
+        // ---- mask in place: element e of subtile ks is key slot
         //      ks*32 + (e/4)*8 + half*4 + e%4 of this block ----------------------------
-        float x[2][16];
-        if (is_list) {
+        const bool list_full =
+            is_list && __builtin_amdgcn_readfirstlane(lfull[min(lb, kMaxList / 64 - 1)]);
+        if (is_list && !list_full) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int t0 = ks * 32 + e4 * 8 + half * 4;
-                    const u32x4 ent = *reinterpret_cast<const u32x4*>(&lst[blk * 64 + t0]);
+                    const u32x4 ent = *reinterpret_cast<const u32x4*>(&lst[lb * 64 + t0]);
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        x[ks][e4 * 4 + u] = (ent[u] <= lim) ? sacc[ks][e4 * 4 + u] : -INFINITY;
+                        if (!(ent[u] <= lim)) sacc[ks][e4 * 4 + u] = -INFINITY;
                 }
             }
-        } else {
-            const bool full = (jb0 >= i_last - w + 1) && (jb0 + 63 <= i0);
-            if (full) {
+        } else if (!is_list) {
+            // d = irow - j: visible iff 0 <= d < w, or d >= w and j passes (sink
+            // ranks read -1); band blocks past kBr keys hold no d >= w
+            const bool causal_ok = jb0 + 63 <= i0;           // d >= 0 on every row
+            const bool in_window = jb0 >= i_last - w + 1;    // d < w on every row
+            const int dbase = irow - jb0 - half * 4;
+            if (causal_ok && !in_window) {
+                const int rb = min(blk, kBr / 64 - 1) * 64;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const int t0 = ks * 32 + e4 * 8 + half * 4;
+                        const int4 br = *reinterpret_cast<const int4*>(&brank[rb + t0]);
+                        const int bv[4] = {br.x, br.y, br.z, br.w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int d = dbase - (ks * 32 + e4 * 8 + u);
+                            if (!((d < w) | (bv[u] <= thr_row))) sacc[ks][e4 * 4 + u] = -INFINITY;
+                        }
+                    }
+                }
+            } else if (in_window && !causal_ok) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) x[ks][e] = sacc[ks][e];
-            } else {
-                // d = irow - j: visible iff 0 <= d < w, or d >= w and j passes
-                // (sink ranks read -1); blocks past the second hold no d >= w
-                const int rb = min(blk - nlist, 1) * 64;
-                const int dbase = irow - jb0 - half * 4;
+                    for (int e = 0; e < 16; ++e) {
+                        const int d = dbase - (ks * 32 + (e >> 2) * 8 + (e & 3));
+                        if (d < 0) sacc[ks][e] = -INFINITY;
+                    }
+            } else if (!in_window) {
+                const int rb = min(blk, kBr / 64 - 1) * 64;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -265,42 +313,47 @@ __global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
                             const int d = dbase - (ks * 32 + e4 * 8 + u);
                             const bool vis = (unsigned(d) < unsigned(w)) |
                                              ((d >= 0) & (bv[u] <= thr_row));
-                            x[ks][e4 * 4 + u] = vis ? sacc[ks][e4 * 4 + u] : -INFINITY;
+                            if (!vis) sacc[ks][e4 * 4 + u] = -INFINITY;
                         }
                     }
                 }
             }
         }
 
-        // ---- online softmax in raw logits (scale folded into the exponent; row =
-        //      this lane's query, keys split with lane^32) ------------------------------
-        float mloc = x[0][0];
+        // ---- online softmax in raw logits, scale folded into the exponent; row =
+        //      this lane's query, keys split with lane^32.  The reference maximum
+        //      m_run moves only when a row's maximum exceeds it by more than 2^8 in
+        //      the exponent, so p <= 256 and the output is rarely rescaled; the
+        //      final division by l_run cancels the choice of m_run exactly.
+        float mloc = sacc[0][0];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, x[ks][e]);
+            for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[ks][e]);
         const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float m_new = fmaxf(m_run, mrow);
-        const float msafe = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2((m_run - msafe) * csc);
-        const float moff = -msafe * csc;
+        // NaN (both -inf: nothing visible yet) compares false: no move
+        const bool move = (mrow - m_run) * csc > 8.0f;
+        if (__ballot(move) != 0ull) {
+            const float m_new = move ? mrow : m_run;
+            const float alpha = move ? fast_exp2((m_run - m_new) * csc) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+            m_run = m_new;
+        }
+        const float moff = (m_run == -INFINITY) ? 0.0f : -m_run * csc;
         float lsum = 0.0f;
         bf16x8 pf[4];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = fast_exp2(fmaf(x[ks][e], csc, moff));
+                const float p = fast_exp2(fmaf(sacc[ks][e], csc, moff));
                 lsum += p;
                 pf[ks * 2 + (e >> 3)][e & 7] = (__bf16)p;
             }
         }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-        if (__ballot(alpha != 1.0f) != 0ull) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
-        }
+        l_run += lsum;
 
         // ---- O^T += V^T P^T ------------------------------------------------------
         // operand element e of lane (16-group G, index i) is V[key][dt*32 + (G&1)*16 + i]
@@ -317,8 +370,9 @@ __global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
                     const int i = lane & 15;
                     const int key = cc * 16 + 8 * r + 4 * (grp >> 1) + (i >> 2);
                     const int d0 = dt * 32 + (grp & 1) * 16 + 4 * (i & 3);
-                    const int chunk = (d0 >> 3) ^ swz(key);
-                    const __bf16* src = reinterpret_cast<const __bf16*>(&Vs[key * CPR + chunk]) + (d0 & 7);
+                    const int chunk = (d0 >> 3) ^ swz<D>(key);
+                    const __bf16* src =
+                        reinterpret_cast<const __bf16*>(&VC[key * CPR + chunk]) + (d0 & 7);
                     typedef short v4i16 __attribute__((ext_vector_type(4)));
                     const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) v4i16*)(src));
@@ -331,14 +385,14 @@ __global__ __launch_bounds__(256, 2) void attend_prefill_kernel(
                 acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[cc], acc_o[dt], 0, 0, 0);
             }
         }
-        __syncthreads();                          // every wave is done with the tiles
-        if (blk + 1 < nblk) {
-            LTE_STAGE()
-            __syncthreads();
-        }
+        __builtin_amdgcn_s_waitcnt(0);            // this wave's loads of the next block landed
+        __syncthreads();                          // everyone's; and the current tiles are free
+    };
+    for (int blk = 0; blk < nblk; blk += 2) {
+        step(blk, K0, V0, K1, V1);
+        if (blk + 1 < nblk) step(blk + 1, K1, V1, K0, V0);
     }
-#undef LTE_FETCH
-#undef LTE_STAGE
+#undef LTE_ISSUE
 
     // ---- normalise and store: element e of d-tile dt is dim dt*32 + (e/4)*8 + half*4 + e%4
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -363,12 +417,12 @@ hipError_t launch_attend_d(const Shape& sh, int64_t T, const uint16_t* q, const 
                            const uint16_t* v, const int32_t* rank, const int32_t* thr,
                            uint16_t* out, hipStream_t st) {
     const int G = sh.G;
-    const int P = 128 / G;
+    const int P = 256 / G;
     const int ntile = int((T + P - 1) / P);
     dim3 grid(unsigned(long(sh.B) * sh.Hkv * ntile));
 #define LTE_ATTEND_CASE(GG)                                                                   \
     case GG:                                                                                  \
-        hipLaunchKernelGGL((attend_prefill_kernel<D, GG>), grid, dim3(256), 0, st, int(T),    \
+        hipLaunchKernelGGL((attend_prefill_kernel<D, GG>), grid, dim3(512), 0, st, int(T),    \
                            sh.Hq, sh.Hkv, sh.s, sh.w, ntile, q, k, v, rank, thr, out);        \
         break;
     switch (G) {

@@ -54,6 +54,7 @@ BASE = dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, sink=4, window=32, cap
     ({"q_heads": 64, "kv_heads": 2}, 2),      # G = 32
     ({"hidden": 16}, 2),
     ({"batch": 0}, 1),
+    ({"q_heads": 256, "kv_heads": 256}, 2),   # 32-bit row offsets
 ])
 def test_config_checks(change, code):
     c = lte.Config(**{**BASE, **change})
