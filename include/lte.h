@@ -105,10 +105,12 @@ typedef struct {
  *                                  slot it takes, -1 if it is not kept, -2
  *                                  if it would leave unscored
  *   nx_score    fp32  [B][Hkv]     that token's score
+ *   arrive      int32 [B][Hkv]     split arrivals of the decode call in
+ *                                  progress; 0 between calls
  *   total       size of the blob in bytes                                */
 typedef struct {
     size_t k, v, ret_idx, ret_score, ring_score, count, pos, next_unscored, flags, weak, nx_slot,
-        nx_score, total;
+        nx_score, arrive, total;
 } lte_cache_layout;
 
 /* Byte offsets inside a prefill workspace for T tokens (intermediates that
@@ -149,8 +151,8 @@ size_t lte_workspace_bytes(const lte_config* cfg, int64_t T);
 int lte_workspace_get_layout(const lte_config* cfg, int64_t T, lte_workspace_layout* out);
 
 /* Resets a cache to the empty state: pos = 0, count = 0, every ring score
- * NaN, flags 0, weak -1, nx_slot -1.  K/V slots are left as they are (never
- * read while invalid). */
+ * NaN, flags 0, weak -1, nx_slot -1, arrive 0.  K/V slots are left as they
+ * are (never read while invalid). */
 int lte_cache_init(const lte_config* cfg, void* cache, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -205,16 +207,17 @@ int lte_score_evict(const lte_config* cfg, const lte_cnn* cnn, const uint16_t* k
 /* Attention of the newest token's queries q_t (bf16 [B][Hq][D]) over the
  * cache: sink U retained segment U ring, out_t bf16 [B][Hq][D].  Requires
  * pos >= 1 (LTE_ERR_STATE is not detectable on the host: a cache with
- * pos == 0 yields zeros). */
-int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, const void* cache,
+ * pos == 0 yields zeros).  The cache's arrive words are used during the
+ * call and left at 0; nothing else in the cache changes. */
+int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, void* cache,
                       void* workspace, size_t workspace_bytes, uint16_t* out_t, void* stream);
 
 /* One decode step, with the result of lte_score_evict followed by
- * lte_decode_attend: the splits of the cache are read in their pre-step
- * state with the new token and the segment slot the leaving token takes
- * substituted; a second launch merges the partial softmax sums in a fixed
- * order and then updates the cache.  Calls that use one cache must be
- * ordered on one stream. */
+ * lte_decode_attend, in one launch: the splits of the cache (64 slots each)
+ * are read in their pre-step state with the new token and the segment slot
+ * the leaving token takes substituted; the last split of a (batch, KV head)
+ * to finish merges the partial softmax sums in split order and then updates
+ * the cache.  Calls that use one cache must be ordered on one stream. */
 int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* k_t,
                     const uint16_t* v_t, const lte_cnn* cnn, void* cache, void* workspace,
                     size_t workspace_bytes, uint16_t* out_t, void* stream);

@@ -231,7 +231,7 @@ int lte_score_evict(const lte_config* cfg, const lte_cnn* cnn, const uint16_t* k
         launch_score_evict(sh, *cnn, k_t, v_t, cache_view(sh, cache), hipStream_t(stream)));
 }
 
-int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, const void* cache,
+int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, void* cache,
                       void* workspace, size_t workspace_bytes, uint16_t* out_t, void* stream) {
     LTE_TRY(check_cfg(cfg));
     if (!q_t || !cache || !out_t) return LTE_ERR_INVALID_ARG;
@@ -239,8 +239,8 @@ int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, const void* ca
     if (workspace == nullptr) return LTE_ERR_INVALID_ARG;
     if (workspace_bytes < ws_layout(sh, 0).total) return LTE_ERR_WORKSPACE;
     return hip_status(launch_decode(sh, false, q_t, nullptr, nullptr, nullptr,
-                                    cache_view(sh, const_cast<void*>(cache)),
-                                    dec_part_ptr(sh, workspace), out_t, hipStream_t(stream)));
+                                    cache_view(sh, cache), dec_part_ptr(sh, workspace), out_t,
+                                    hipStream_t(stream)));
 }
 
 int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* k_t,

@@ -32,6 +32,7 @@ __global__ void cache_init_kernel(int BG, int w, int s, CacheView c) {
         c.weak[x] = -1;
         c.nx_slot[x] = -1;
         c.nx_score[x] = 0.0f;
+        c.arrive[x] = 0;
     }
 }
 
@@ -146,6 +147,7 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int T, int s, int w, in
         }
         c.nx_slot[bg] = nx;
         c.nx_score[bg] = rl;
+        c.arrive[bg] = 0;
     }
 }
 

@@ -25,28 +25,33 @@
 // so whoever finishes an ingest (or builds the cache) also records the next
 // one (nx_slot, nx_score): the attention of a step never waits for it.
 //
-// A decode step is two launches and no device-scope fence:
-//   decode_split_kernel   one wave per 64 cache slots, reading them in the
-//       PRE-step state with the post-ingest contents substituted: ring slot
-//       t mod w (and sink slot t) come from the k_t/v_t inputs, and the
-//       segment slot the leaving token takes reads that token from its ring
-//       slot (that wave also copies the row into the slot: no other wave
-//       reads it).  q.k and p.v run on v_mfma_f32_16x16x32_bf16 with the
-//       G <= 16 query heads of the KV head as the 16 columns; the wave writes
-//       (max, sum, unnormalised o) per head.
-//   decode_finish_kernel  one workgroup per (batch, KV head): merges the
-//       partials in split order (deterministic), writes o_t, then applies the
-//       rest of the ingest and records the next decision.
-// (Merging inside one launch would need an agent-scope fence per workgroup,
-// which on gfx950 writes back and invalidates the XCD's L2.)
+// A decode step is one launch of one-wave workgroups, one per 64 cache
+// slots of a (batch, KV head):
+//   * each reads its slots in the PRE-step state with the post-ingest
+//     contents substituted: ring slot t mod w (and sink slot t) come from the
+//     k_t/v_t inputs, and the segment slot the leaving token takes reads that
+//     token from its ring slot (that wave also copies the row into the slot:
+//     no other wave reads it).  K rows go straight into MFMA operand
+//     registers; V rows are loaded into LDS by direct global->LDS loads and
+//     read back transposed (ds_read_b64_tr_b16).  q.k and p.v run on
+//     v_mfma_f32_16x16x32_bf16 with the G <= 16 query heads of the KV head
+//     as the 16 columns;
+//   * on a scoring step the waves of a (batch, KV head) share the deferred
+//     batch, 28 tokens per wave call;
+//   * each wave writes (max, sum, unnormalised o) per head with device-scope
+//     coherent stores and counts itself in on the (batch, KV head)'s arrival
+//     word; the last to arrive merges the partials in split order
+//     (deterministic), writes o_t, applies the rest of the ingest, records
+//     the next decision and clears the arrival word.  The partials bypass
+//     the non-coherent L2 copies instead of a cache-wide write-back and
+//     invalidate, which a device-scope fence would cost on gfx950.
 #include "score_core.h"
 
 namespace lte {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxG = 16;
-constexpr int KPB = kDecodeSplitKeys;          // cache slots per split (64)
+constexpr int KPB = kDecodeSplitKeys;          // cache slots per wave (64)
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]
 // and D[4(l/16)+r][l%16].
@@ -54,17 +59,22 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Position of key k (0..63 within a split) in the V^T rows: keys are permuted
-// inside each 32-key chunk so that lane group q of the P.V MFMA reads its 8
-// keys {4q..4q+3, 16+4q..16+4q+3} -- the rows of the q.k output it holds --
-// as one 16-byte run.
-__device__ __forceinline__ int vt_pos(int k) {
-    const int cc = k >> 5;
-    const int kc = k & 31;
-    const int hi = kc >> 4;            // second 16-key tile of the chunk
-    const int q = (kc & 15) >> 2;
-    const int e = (kc & 3) + 4 * hi;
-    return 32 * cc + 8 * q + e;
+// LDS chunk swizzle of V tile row r: 16-byte chunk c of row r sits at chunk
+// position c ^ swz(r).  A transposing read of the p.v operand fetches chunks
+// 2dt, 2dt+1 of 4 consecutive rows per 16 lanes (8 rows per 32 lanes); with
+// swz = 2 (r mod 8) (D = 128) or 2 (r mod 4) (D = 64) those land on distinct
+// bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? 2 * (r & 7) : 2 * (r & 3); }
+
+// Device-scope coherent traffic for the split partials: buffer loads and
+// stores with the sc1 cache-policy bit, the bit relaxed agent-scope atomic
+// loads and stores carry, in 16-byte pieces.  Offsets in bytes.
+constexpr int kSc1 = 16;                       // cache-policy operand: sc1
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, 0x7fffffff, 0x00020000);
 }
 
 // Decision for the token leaving at the ingest of position t, from the state
@@ -79,177 +89,155 @@ __device__ __forceinline__ int decide_slot(int64_t t, float rl, int cnt, int wea
     return -1;
 }
 
-// Finishes an ingest of token t in the cache of one (b, g), given the state
-// the caller read before any write (cnt, X = nx_slot, rl = nx_score, u, wk,
-// wscore = ret_score[wk]).  Run by one whole workgroup of 256 threads.
-// copy_row: also move the leaving token's row into segment slot X (the
-// split kernel did it already on the decode-step path).
+// Scores chunk ch (tokens u + 28 ch .. u + 28 ch + 27, clipped to t-2) of the
+// deferred batch of (b, g) at step t, reading tokens < t from their ring slots
+// and token t from the inputs.  One wave.
 template <int D>
-__device__ void ingest_finish(const CacheView& c, int bg, int g, int s, int w, int C, int S,
-                              int64_t t, int cnt, int X, float rl, int64_t u, int wk, float wscore,
-                              bool copy_row, const uint16_t* __restrict__ k_t,
-                              const uint16_t* __restrict__ v_t, const lte_cnn& cnn,
-                              unsigned char* smem, float* w2s, float* red_s, int* red_t,
-                              int* red_x) {
-    constexpr int KK = ScoreSmem<D>::KK;
-    constexpr int NW = ScoreSmem<D>::NW;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int tslot = int(t % w);
-    const int ring0 = s + C;
-    const long ring_row = (long(bg) * S + ring0 + tslot) * D;
-    const int64_t jl = t - w;
-    const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
-    // score of token t+1-w, which leaves at the next ingest: scored at least three
-    // steps before it leaves, never by this step's batch
-    const int64_t t1 = t + 1;
-    const float r1 = (t1 - w >= s) ? c.ring_score[long(bg) * w + int(t1 % w)] : 0.0f;
+__device__ void score_deferred_chunk(const CacheView& c, int bg, int g, int s, int w, int C,
+                                     int S, int t, int u, int ch,
+                                     const uint16_t* __restrict__ k_t,
+                                     const uint16_t* __restrict__ v_t, const lte_cnn& cnn,
+                                     float* Y) {
+    const uint16_t* kring = c.k + (long(bg) * S + s + C) * D;
+    const uint16_t* vring = c.v + (long(bg) * S + s + C) * D;
+    float* rs = c.ring_score + long(bg) * w;
+    score_wave<D>(
+        Y, cnn.w1 + long(g) * kHidden * 2 * D * 3, cnn.b1 + g * kHidden,
+        cnn.w2 + g * kHidden * 3, cnn.b2[g], u + kWaveScoreTile * ch, u, t - 2,
+        [&](int x, const uint16_t*& kp, const uint16_t*& vp) {
+            if (x < 0 || x > t) return false;
+            if (x == t) {
+                kp = k_t + long(bg) * D;
+                vp = v_t + long(bg) * D;
+            } else {
+                kp = kring + long(x % w) * D;
+                vp = vring + long(x % w) * D;
+            }
+            return true;
+        },
+        [&](int x) { return x < 0; },
+        [&](int tok, float r) { rs[tok % w] = r; });
+}
 
-    if (tid < D / 8) {       // same thread reads the ring chunk before overwriting it
-        const int ch = tid;
-        const uint4 kv = *reinterpret_cast<const uint4*>(k_t + long(bg) * D + ch * 8);
-        const uint4 vv = *reinterpret_cast<const uint4*>(v_t + long(bg) * D + ch * 8);
-        if (copy_row && X >= 0) {
-            const uint4 lk = *reinterpret_cast<const uint4*>(c.k + ring_row + ch * 8);
-            const uint4 lv = *reinterpret_cast<const uint4*>(c.v + ring_row + ch * 8);
-            const long dst = (long(bg) * S + s + X) * D + ch * 8;
-            *reinterpret_cast<uint4*>(c.k + dst) = lk;
-            *reinterpret_cast<uint4*>(c.v + dst) = lv;
-        }
-        *reinterpret_cast<uint4*>(c.k + ring_row + ch * 8) = kv;
-        *reinterpret_cast<uint4*>(c.v + ring_row + ch * 8) = vv;
+// Order of segment entries for eviction: a is weaker than b when its score is
+// lower, or equal with the higher token index.
+__device__ __forceinline__ bool weaker(float sa, int ta, float sb, int tb) {
+    return sa < sb || (sa == sb && ta > tb);
+}
+
+// Weakest of (score, token, slot) over the wave; lanes without an entry hold
+// (+inf, -1, -1).
+__device__ __forceinline__ void wave_weakest(float& sc, int& tk, int& sl) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float os = __shfl_xor(sc, o, 64);
+        const int ot = __shfl_xor(tk, o, 64);
+        const int ol = __shfl_xor(sl, o, 64);
+        if (weaker(os, ot, sc, tk)) { sc = os; tk = ot; sl = ol; }
+    }
+}
+
+// Writes of the ingest of token t into the cache of one (b, g), from the
+// state before the step (cnt, X = nx_slot, rl = nx_score, u) and what the
+// step computed: (wk, ws) the weakest slot and score of the post-step
+// segment when it holds C entries (else wk = -1), r1 the score of token
+// t+1-w, which leaves at the next ingest (scored at least three steps before
+// it leaves, never by this step's batch), and the new token's 16-byte chunk
+// `lane` of k and v for lanes < D/8.  One wave.
+template <int D>
+__device__ void ingest_commit(const CacheView& c, int bg, int s, int w, int C, int S, int t,
+                              int cnt, int X, float rl, int u, int wk, float ws, float r1,
+                              const u32x4& nk, const u32x4& nv) {
+    const int lane = threadIdx.x & 63;
+    const int tslot = t % w;
+    const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
+    if (lane < D / 8) {
+        const long ring_row = (long(bg) * S + s + C + tslot) * D + lane * 8;
+        *reinterpret_cast<u32x4*>(c.k + ring_row) = nk;
+        *reinterpret_cast<u32x4*>(c.v + ring_row) = nv;
         if (t < s) {
-            const long srow = (long(bg) * S + t) * D + ch * 8;
-            *reinterpret_cast<uint4*>(c.k + srow) = kv;
-            *reinterpret_cast<uint4*>(c.v + srow) = vv;
+            const long srow = (long(bg) * S + t) * D + lane * 8;
+            *reinterpret_cast<u32x4*>(c.k + srow) = nk;
+            *reinterpret_cast<u32x4*>(c.v + srow) = nv;
         }
     }
-    if (tid == 0) {
+    if (lane == 0) {
         if (X >= 0) {
-            c.ret_idx[long(bg) * C + X] = int(jl);
+            c.ret_idx[long(bg) * C + X] = t - w;
             c.ret_score[long(bg) * C + X] = rl;
             c.count[bg] = new_cnt;
         }
         if (X == -2) c.flags[bg] |= 1;
         c.ring_score[long(bg) * w + tslot] = __builtin_nanf("");
-    }
-
-    // weakest entry of a full segment, with slot X already holding the newcomer
-    int wk2 = wk;
-    float ws2 = wscore;
-    if (X >= 0 && new_cnt == C) {
-        float bs = INFINITY;
-        int bt = -1, bx = -1;
-        for (int x = tid; x < C; x += 256) {
-            float sc;
-            int tk;
-            if (x == X) {
-                sc = rl;
-                tk = int(jl);
-            } else {
-                sc = c.ret_score[long(bg) * C + x];
-                tk = c.ret_idx[long(bg) * C + x];
-            }
-            if (sc < bs || (sc == bs && tk > bt)) { bs = sc; bt = tk; bx = x; }
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float os = __shfl_xor(bs, o, 64);
-            const int ot = __shfl_xor(bt, o, 64);
-            const int ox = __shfl_xor(bx, o, 64);
-            if (os < bs || (os == bs && ot > bt)) { bs = os; bt = ot; bx = ox; }
-        }
-        if (lane == 0) { red_s[wave] = bs; red_t[wave] = bt; red_x[wave] = bx; }
-        __syncthreads();
-        bs = red_s[0]; bt = red_t[0]; bx = red_x[0];
-#pragma unroll
-        for (int q = 1; q < 4; ++q) {
-            if (red_s[q] < bs || (red_s[q] == bs && red_t[q] > bt)) {
-                bs = red_s[q]; bt = red_t[q]; bx = red_x[q];
-            }
-        }
-        wk2 = bx;
-        ws2 = bs;
-        if (tid == 0) c.weak[bg] = bx;
-    }
-
-    int64_t u2 = u;
-    if (t == u + w - 3) {                             // deferred batched scoring
-        __threadfence_block();
-        __syncthreads();                              // ring row of token t written
-        for (int x = tid; x < kHidden * 3; x += 256) w2s[x] = cnn.w2[g * kHidden * 3 + x];
-        const uint16_t* kring = c.k + (long(bg) * S + ring0) * D;
-        const uint16_t* vring = c.v + (long(bg) * S + ring0) * D;
-        float* rs = c.ring_score + long(bg) * w;
-        const int tt = int(t);
-        for (int t0 = int(u); t0 <= tt - 2; t0 += kScoreTile) {
-            bf16x8* wl = reinterpret_cast<bf16x8*>(smem);     // W1 as packed bf16 operands
-            for (int x = tid; x < NW; x += 256) {
-                int tap, kk, ln;
-                w1p_coords(x, KK, tap, kk, ln);
-                const float* src = cnn.w1 +
-                    ((long(g) * kHidden + ln % 32) * (2 * D) + kk * 16 + (ln / 32) * 8) * 3 + tap;
-                bf16x8 e8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) e8[e] = (__bf16)src[e * 3];
-                wl[x] = e8;
-            }
-            score_chunk<D>(
-                smem, w2s, cnn.b1 + g * kHidden, cnn.b2[g], t0, int(u), tt - 2,
-                [&](int x, const uint16_t*& kp, const uint16_t*& vp) {
-                    if (x < 0 || x > tt) return false;
-                    kp = kring + long(x % w) * D;
-                    vp = vring + long(x % w) * D;
-                    return true;
-                },
-                [&](int x) { return x < 0; },
-                [&](int tok, float r) { rs[tok % w] = r; });
-        }
-        u2 = t - 1;
-    }
-    // the next ingest's decision
-    if (tid == 0) {
-        c.nx_slot[bg] = decide_slot(t1, r1, new_cnt, wk2, ws2, s, w, C);
+        c.weak[bg] = wk;
+        c.nx_slot[bg] = decide_slot(t + 1, r1, new_cnt, wk, ws, s, w, C);
         c.nx_score[bg] = r1;
-        c.next_unscored[bg] = u2;
-        c.pos[bg] = t1;
+        c.next_unscored[bg] = (t == u + w - 3) ? t - 1 : u;
+        c.pos[bg] = t + 1;
     }
 }
 
+// lte_score_evict: the ingest alone, one wave per (batch, KV head).
 template <int D>
-__global__ __launch_bounds__(256) void score_evict_kernel(int s, int w, int C, int S, int Hkv,
-                                                          const uint16_t* __restrict__ k_t,
-                                                          const uint16_t* __restrict__ v_t,
-                                                          lte_cnn cnn, CacheView c) {
-    __shared__ __align__(16) unsigned char smem[ScoreSmem<D>::kBytes];
-    __shared__ float w2s[kHidden * 3];
-    __shared__ float red_s[4];
-    __shared__ int red_t[4], red_x[4];
+__global__ __launch_bounds__(64) void score_evict_kernel(int s, int w, int C, int S, int Hkv,
+                                                         const uint16_t* __restrict__ k_t,
+                                                         const uint16_t* __restrict__ v_t,
+                                                         lte_cnn cnn, CacheView c) {
+    __shared__ __align__(16) float Y[kWaveScoreBytes / 4];
+    const int lane = threadIdx.x;
     const int bg = blockIdx.x;
-    const int64_t t = c.pos[bg];
+    const int t = int(c.pos[bg]);
     const int cnt = c.count[bg];
     const int X = c.nx_slot[bg];
     const float rl = c.nx_score[bg];
-    const int64_t u = c.next_unscored[bg];
-    const int wk = c.weak[bg];
-    const float ws = (wk >= 0) ? c.ret_score[long(bg) * C + wk] : 0.0f;
-    __syncthreads();                       // every thread has read the pre-step state
-    ingest_finish<D>(c, bg, bg % Hkv, s, w, C, S, t, cnt, X, rl, u, wk, ws, true, k_t, v_t, cnn,
-                     smem, w2s, red_s, red_t, red_x);
+    const int u = int(c.next_unscored[bg]);
+    const int tslot = t % w;
+    const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
+    const float r1 = (t + 1 - w >= s) ? c.ring_score[long(bg) * w + (t + 1) % w] : 0.0f;
+    u32x4 nk = u32x4{}, nv = u32x4{};
+    if (lane < D / 8) {
+        nk = *reinterpret_cast<const u32x4*>(k_t + long(bg) * D + lane * 8);
+        nv = *reinterpret_cast<const u32x4*>(v_t + long(bg) * D + lane * 8);
+        if (X >= 0) {                         // the leaving token's row into its slot
+            const long rr = (long(bg) * S + s + C + tslot) * D + lane * 8;
+            const long dst = (long(bg) * S + s + X) * D + lane * 8;
+            *reinterpret_cast<u32x4*>(c.k + dst) = *reinterpret_cast<const u32x4*>(c.k + rr);
+            *reinterpret_cast<u32x4*>(c.v + dst) = *reinterpret_cast<const u32x4*>(c.v + rr);
+        }
+    }
+    // weakest entry of the post-step segment when full, slot X holding the newcomer
+    float wsc = INFINITY;
+    int wtk = -1, wsl = -1;
+    if (C > 0 && new_cnt == C) {
+        for (int x = lane; x < C; x += 64) {
+            const float sc = (x == X) ? rl : c.ret_score[long(bg) * C + x];
+            const int tk = (x == X) ? t - w : c.ret_idx[long(bg) * C + x];
+            if (weaker(sc, tk, wsc, wtk)) { wsc = sc; wtk = tk; wsl = x; }
+        }
+        wave_weakest(wsc, wtk, wsl);
+    }
+    if (t == u + w - 3) {                     // deferred batch: ring rows of tokens < t
+        const int nch = (t - 1 - u + kWaveScoreTile - 1) / kWaveScoreTile;
+        for (int ch = 0; ch < nch; ++ch)
+            score_deferred_chunk<D>(c, bg, bg % Hkv, s, w, C, S, t, u, ch, k_t, v_t, cnn, Y);
+    }
+    __builtin_amdgcn_s_waitcnt(0);            // ring row copied before it is overwritten
+    ingest_commit<D>(c, bg, s, w, C, S, t, cnt, X, rl, u, wsl, wsc, r1, nk, nv);
 }
 
-// Attention partials of one split of 64 cache slots; one wave.
-template <int D, bool INGEST>
-__global__ __launch_bounds__(64) void decode_split_kernel(
-    int Hq, int Hkv, int G, int s, int w, int C, int S, int nsplit,
+// One decode step (INGEST) or an attention over the cache as it is.
+template <int D, int G, bool INGEST>
+__global__ __launch_bounds__(64, 3) void decode_step_kernel(
+    int Hq, int Hkv, int s, int w, int C, int S, int nsplit,
     const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
-    const uint16_t* __restrict__ v_t, CacheView c, float* __restrict__ part) {
+    const uint16_t* __restrict__ v_t, lte_cnn cnn, CacheView c, float* __restrict__ part,
+    uint16_t* __restrict__ out_t) {
     constexpr int KS = D / 32;                 // q.k k-steps
     constexpr int DT = D / 16;                 // p.v output tiles
-    constexpr int NU = D / 32;                 // V transpose units per lane
-    constexpr int VST = KPB + 8;               // V^T row stride (bf16), padded
-    __shared__ __align__(16) __bf16 Vt[D * VST];
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int kVBytes = KPB * CPR * 16;
+    constexpr int kBuf = kVBytes > kWaveScoreBytes ? kVBytes : kWaveScoreBytes;
+    __shared__ __align__(16) u32x4 Vs[kBuf / 16];     // V tile; later the scorer's rows
 
     const int lane = threadIdx.x;
     const int l16 = lane & 15;
@@ -259,11 +247,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int b = bg / Hkv;
     const int g = bg % Hkv;
     const int slot0 = sp * KPB;
-
     const long base = long(bg) * S * D;
 
-    // ---- bulk loads first: q (B operand), and every slot's row of the cache as it
-    //      is (A operands of q.k; V transpose units) -- none waits for the state ----
+    // ---- bulk loads first: the V tile (direct to LDS), q (B operand) and the K
+    //      rows (A operands of q.k), in the pre-step state -------------------------------
+#pragma unroll
+    for (int x = 0; x < CPR; ++x) {
+        const int cidx = 64 * x + lane;
+        const int row = cidx / CPR;
+        const int gch = (cidx % CPR) ^ vswz<D>(row);
+        const uint16_t* src = c.v + base + long(min(slot0 + row, S - 1)) * D + gch * 8;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(&Vs[64 * x]),
+                                         16, 0, 0);
+    }
     bf16x8 qf[KS];
     {
         const bool hv = l16 < G;
@@ -280,37 +277,50 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         for (int kk = 0; kk < KS; ++kk)
             ka[mt][kk] = *reinterpret_cast<const bf16x8*>(r + 32 * kk + 8 * q16);
     }
-    uint4 vr[NU][4];
-#pragma unroll
-    for (int uu = 0; uu < NU; ++uu) {
-        const int U = lane + 64 * uu;
-        const int kg = U / (D / 8);            // 4 keys 4kg .. 4kg+3
-        const int dg = U % (D / 8);            // 8 dims 8dg .. 8dg+7
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
-            vr[uu][k4] = *reinterpret_cast<const uint4*>(
-                c.v + base + long(min(slot0 + 4 * kg + k4, S - 1)) * D + 8 * dg);
-    }
 
     // ---- the state, loaded alongside (positions fit in 32 bits) ----------------------
     const int p = int(c.pos[bg]);
     const int cnt = c.count[bg];
     const int X = INGEST ? c.nx_slot[bg] : -1;
+    const int u = INGEST ? int(c.next_unscored[bg]) : 0;
+    const float rl = INGEST ? c.nx_score[bg] : 0.0f;
     const int t = INGEST ? p : p - 1;
     const int tslot = t >= 0 ? t % w : 0;
     const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
+    // ingest operands every wave fetches (the last to arrive commits them): the new
+    // token's row chunk, the score of the token leaving next, and the weakest of this
+    // split's segment entries in the post-step state (slot X holding the newcomer)
+    u32x4 nk = u32x4{}, nv = u32x4{};
+    float r1 = 0.0f;
+    float wsc = INFINITY;
+    int wtk = -1, wsl = -1;
+    if (INGEST) {
+        if (lane < CPR) {
+            nk = *reinterpret_cast<const u32x4*>(k_t + long(bg) * D + lane * 8);
+            nv = *reinterpret_cast<const u32x4*>(v_t + long(bg) * D + lane * 8);
+        }
+        if (t + 1 - w >= s) r1 = c.ring_score[long(bg) * w + (t + 1) % w];
+        const int e = slot0 + lane - s;
+        if (C > 0 && new_cnt == C && e >= 0 && e < C) {
+            wsc = (e == X) ? rl : c.ret_score[long(bg) * C + e];
+            wtk = (e == X) ? t - w : c.ret_idx[long(bg) * C + e];
+            wsl = e;
+        }
+    }
 
     // rows that differ in the post-ingest state: the new token (ring slot t mod w and,
     // while t < s, sink slot t) comes from the inputs; segment slot X holds the leaving
     // token, still in ring slot t mod w.  At most three slots, each checked once.
+    int fs[3] = {-1, -1, -1};
     if (INGEST) {
-        const int fs[3] = {t < s ? t : -1, X >= 0 ? s + X : -1, s + C + tslot};
+        fs[0] = t < s ? t : -1;
+        fs[1] = X >= 0 ? s + X : -1;
+        fs[2] = s + C + tslot;
 #pragma unroll
         for (int f = 0; f < 3; ++f) {
             const int kk = fs[f] - slot0;                     // wave-uniform
             if (fs[f] < 0 || kk < 0 || kk >= KPB || fs[f] >= S) continue;
             const uint16_t* rk = (f == 1) ? c.k + base + long(s + C + tslot) * D : k_t + long(bg) * D;
-            const uint16_t* rv = (f == 1) ? c.v + base + long(s + C + tslot) * D : v_t + long(bg) * D;
             if (l16 == (kk & 15)) {                           // q.k A operand rows
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
@@ -318,19 +328,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
                         for (int kq = 0; kq < KS; ++kq)
                             ka[mt][kq] = *reinterpret_cast<const bf16x8*>(rk + 32 * kq + 8 * q16);
-                    }
-                }
-            }
-#pragma unroll
-            for (int uu = 0; uu < NU; ++uu) {                 // V transpose units
-                const int U = lane + 64 * uu;
-                if (U / (D / 8) == (kk >> 2)) {
-                    const uint4 nv = *reinterpret_cast<const uint4*>(rv + 8 * (U % (D / 8)));
-                    switch (kk & 3) {
-                        case 0: vr[uu][0] = nv; break;
-                        case 1: vr[uu][1] = nv; break;
-                        case 2: vr[uu][2] = nv; break;
-                        default: vr[uu][3] = nv; break;
                     }
                 }
             }
@@ -355,7 +352,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         }
         vmask = __ballot(ok);
     }
-    auto valid = [&](int k) -> bool { return (vmask >> k) & 1ull; };
 
     // the wave owning the slot the leaving token takes also moves its row there
     if (INGEST && X >= 0) {
@@ -365,26 +361,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             const long dst = base + long(s + X) * D + lane * 8;
             *reinterpret_cast<uint4*>(c.k + dst) = *reinterpret_cast<const uint4*>(c.k + rr);
             *reinterpret_cast<uint4*>(c.v + dst) = *reinterpret_cast<const uint4*>(c.v + rr);
-        }
-    }
-
-    // ---- V^T into LDS ----------------------------------------------------------------
-#pragma unroll
-    for (int uu = 0; uu < NU; ++uu) {
-        const int U = lane + 64 * uu;
-        const int kg = U / (D / 8);
-        const int dg = U % (D / 8);
-        const int pos = vt_pos(4 * kg);
-        const uint16_t* r0 = reinterpret_cast<const uint16_t*>(&vr[uu][0]);
-        const uint16_t* r1 = reinterpret_cast<const uint16_t*>(&vr[uu][1]);
-        const uint16_t* r2 = reinterpret_cast<const uint16_t*>(&vr[uu][2]);
-        const uint16_t* r3 = reinterpret_cast<const uint16_t*>(&vr[uu][3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint2 pk;
-            pk.x = uint32_t(r0[e]) | (uint32_t(r1[e]) << 16);
-            pk.y = uint32_t(r2[e]) | (uint32_t(r3[e]) << 16);
-            *reinterpret_cast<uint2*>(&Vt[(8 * dg + e) * VST + pos]) = pk;
         }
     }
 
@@ -403,7 +379,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const bool ok = valid(16 * mt + 4 * q16 + r);
+            const bool ok = (vmask >> (16 * mt + 4 * q16 + r)) & 1ull;
             x[mt][r] = ok ? sacc[mt][r] * csc : -INFINITY;
             m = fmaxf(m, x[mt][r]);
         }
@@ -411,7 +387,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     const float msafe = (m == -INFINITY) ? 0.0f : m;
-    // p = p_hi + p_lo, both bf16: the P.V product keeps ~16 mantissa bits of p
+    // p = p_hi + p_lo, both bf16: the P.V product keeps ~16 mantissa bits of p.
+    // B operand of chunk cc, element e: key 32cc + 16(e/4) + 4q16 + e%4
     float l = 0.0f;
     bf16x8 pf[2], pl[2];
 #pragma unroll
@@ -427,156 +404,170 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    __syncthreads();                                  // V^T complete
 
-    // ---- o^T = V^T p^T: rows = dims 16dt + 4q16 + r, column = head l16 ----------------
+    // ---- V tile landed; substituted rows overwrite theirs --------------------------------
+    __builtin_amdgcn_s_waitcnt(0);
+    if (INGEST) {
+#pragma unroll
+        for (int f = 0; f < 3; ++f) {
+            const int kk = fs[f] - slot0;
+            if (fs[f] < 0 || kk < 0 || kk >= KPB || fs[f] >= S) continue;
+            const uint16_t* rv = (f == 1) ? c.v + base + long(s + C + tslot) * D : v_t + long(bg) * D;
+            if (lane < CPR)
+                Vs[kk * CPR + lane] = *reinterpret_cast<const u32x4*>(rv + 8 * (lane ^ vswz<D>(kk)));
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- o^T = V^T p^T: rows = dims 16dt + 4q16 + r, column = head l16.  A operand
+    //      element e of lane (q16, i): V[32cc + 16(e/4) + 4q16 + e%4][16dt + i], two
+    //      transposing reads of 4 keys; lane j of the 16 reads key .. + j/4, dims
+    //      16dt + 4(j%4) .. +3 --------------------------------------------------------------
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
     f32x4 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         oacc[dt] = f32x4{};
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(&Vt[(16 * dt + l16) * VST + 32 * cc + 8 * q16]);
+            bf16x8 a;
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const int key = 32 * cc + 16 * r2 + 4 * q16 + (l16 >> 2);
+                const int d0 = 16 * dt + 4 * (l16 & 3);
+                const __bf16* src = reinterpret_cast<const __bf16*>(
+                                        &Vs[key * CPR + ((d0 >> 3) ^ vswz<D>(key))]) + (d0 & 7);
+                const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16*)(src));
+                const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[4 * r2 + e] = b4[e];
+            }
             oacc[dt] = mfma16(a, pf[cc], oacc[dt]);
             oacc[dt] = mfma16(a, pl[cc], oacc[dt]);
         }
     }
+    // partial of this split: o [G][D] at 0, (max, sum) of head h at G*D + 2h
+    constexpr int kPart = decode_part_floats(G, D);             // floats per split
+    __amdgpu_buffer_rsrc_t prs = part_rsrc(part + long(bg) * nsplit * kPart);
     if (l16 < G) {
-        float* pb = part + ((long(bg) * nsplit + sp) * G + l16) * (D + 2);
+        const int pbase = sp * kPart * 4;                          // bytes
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 o4 = oacc[dt];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), prs,
+                                                   pbase + (l16 * D + 16 * dt + 4 * q16) * 4, 0,
+                                                   kSc1);
+        }
         if (q16 == 0) {
-            pb[0] = m;
-            pb[1] = l;
+            const f32x2 ml = {m, l};
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), prs,
+                                                  pbase + (G * D + 2 * l16) * 4, 0, kSc1);
         }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pb[2 + 16 * dt + 4 * q16 + r] = oacc[dt][r];
     }
-}
-
-// Merge of the split partials (fixed split order) and, for a decode step, the
-// rest of the ingest.  One workgroup per (batch, KV head).  Every load that
-// does not depend on another is issued first: the state words, k_t/v_t, the
-// segment entries (for a possible weakest-entry search), every split's
-// (max, sum) and the first CH splits' o values.
-template <int D, int G, bool INGEST>
-__global__ __launch_bounds__(256) void decode_finish_kernel(
-    int Hq, int Hkv, int s, int w, int C, int S, int nsplit, const uint16_t* __restrict__ k_t,
-    const uint16_t* __restrict__ v_t, lte_cnn cnn, CacheView c, const float* __restrict__ part,
-    uint16_t* __restrict__ out_t) {
-    constexpr int NO = (G * D + 255) / 256;                  // outputs per thread
-    constexpr int CH = (64 / NO < 2) ? 2 : (64 / NO > 32 ? 32 : 64 / NO);   // splits per round
-    constexpr int kSplitMax = (kMaxSink + kMaxCapacity + 32768 + KPB - 1) / KPB;
-    constexpr int kFw = kSplitMax * G * 4;
-    constexpr int kBuf = (INGEST && ScoreSmem<D>::kBytes > kFw) ? ScoreSmem<D>::kBytes : kFw;
-    __shared__ __align__(16) unsigned char smem[kBuf];       // split weights; later the scorer
-    __shared__ float invL[G];
-    __shared__ float w2s[INGEST ? kHidden * 3 : 1];
-    __shared__ float red_s[4];
-    __shared__ int red_t[4], red_x[4];
-    float* fw = reinterpret_cast<float*>(smem);              // [nsplit][G]
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int bg = blockIdx.x;
-    const int b = bg / Hkv;
-    const int g = bg % Hkv;
-    const long stride = long(G) * (D + 2);                   // floats per split
-    const float* p0 = part + long(bg) * nsplit * stride;
-
-    // ---- round 1 -----------------------------------------------------------------------
-    int64_t t = 0, u = 0;
-    int cnt = 0, X = -1, wk = -1;
-    float rl = 0.0f;
     if (INGEST) {
-        t = c.pos[bg];
-        cnt = c.count[bg];
-        X = c.nx_slot[bg];
-        rl = c.nx_score[bg];
-        u = c.next_unscored[bg];
-        wk = c.weak[bg];
-    }
-    float ov[NO][CH];
-#pragma unroll
-    for (int j = 0; j < NO; ++j) {
-        const int x = tid + 256 * j;
-        const int hh = x / D;
-        const int dd = x % D;
-#pragma unroll
-        for (int q = 0; q < CH; ++q)
-            ov[j][q] = (x < G * D && q < nsplit) ? p0[q * stride + hh * (D + 2) + 2 + dd] : 0.0f;
-    }
-    constexpr int kMl = (kSplitMax + 63) / 64;
-    float mv[(G + 3) / 4][kMl], lv[(G + 3) / 4][kMl];
-#pragma unroll
-    for (int j = 0; j < (G + 3) / 4; ++j) {
-        const int hh = wave + 4 * j;
-#pragma unroll
-        for (int q = 0; q < kMl; ++q) {
-            const int sp = lane + 64 * q;
-            const bool ok = hh < G && sp < nsplit;
-            mv[j][q] = ok ? p0[sp * stride + hh * (D + 2)] : -INFINITY;
-            lv[j][q] = ok ? p0[sp * stride + hh * (D + 2) + 1] : 0.0f;
+        wave_weakest(wsc, wtk, wsl);
+        if (lane == 0) {
+            const u32x4 wt = {__float_as_uint(wsc), uint32_t(wtk), uint32_t(wsl), 0u};
+            __builtin_amdgcn_raw_buffer_store_b128(wt, prs, sp * kPart * 4 + (G * D + 2 * G) * 4,
+                                                   0, kSc1);
         }
     }
 
-    // ---- per head: M = max of the split maxima, weights 2^(m_sp - M), 1/L ---------------
+    // ---- this step's share of the deferred batch ---------------------------------------
+    if (INGEST) {
+        if (t == u + w - 3) {
+            float* Y = reinterpret_cast<float*>(Vs);
+            const int nch = (t - 1 - u + kWaveScoreTile - 1) / kWaveScoreTile;
+            for (int ch = sp; ch < nch; ch += nsplit)
+                score_deferred_chunk<D>(c, bg, g, s, w, C, S, t, u, ch, k_t, v_t, cnn, Y);
+        }
+    }
+
+    // ---- arrival: the last wave of (b, g) merges and finishes the step --------------------
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);            // partials (and row copies) complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(c.arrive + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old != nsplit - 1) return;
+
+    // merge: lane handles head hh = lane / LPH, dims [d0, d0 + DPL), online over the
+    // splits in split order; coherent loads CH splits at a time
+    {
+        constexpr int LPH = 64 / G;               // lanes per head
+        constexpr int DPL = D / LPH;              // dims per lane: 1, 2 or a multiple of 4
+        constexpr int NQ = DPL >= 4 ? DPL / 4 : 1;        // loads of o per split
+        constexpr int CH = 96 / (DPL + 2) > 0 ? 96 / (DPL + 2) : 1;   // splits per round
+        const int hh = lane / LPH;
+        const int d0 = (lane % LPH) * DPL;
+        float M = -INFINITY, L = 0.0f;
+        float o[DPL];
 #pragma unroll
-    for (int j = 0; j < (G + 3) / 4; ++j) {
-        const int hh = wave + 4 * j;
-        if (hh < G) {
-            float M = -INFINITY;
+        for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+        for (int c0 = 0; c0 < nsplit; c0 += CH) {
+            f32x2 ml[CH];
+            f32x4 ov[CH][NQ];
 #pragma unroll
-            for (int q = 0; q < kMl; ++q) M = fmaxf(M, mv[j][q]);
+            for (int q = 0; q < CH; ++q) {
+                const int pb = min(c0 + q, nsplit - 1) * kPart * 4;
+                ml[q] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      prs, pb + (G * D + 2 * hh) * 4, 0, kSc1));
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-            float L = 0.0f;
-#pragma unroll
-            for (int q = 0; q < kMl; ++q) {
-                const int sp = lane + 64 * q;
-                const float f = (mv[j][q] == -INFINITY) ? 0.0f
-                                                         : __builtin_amdgcn_exp2f(mv[j][q] - M);
-                if (sp < nsplit) fw[sp * G + hh] = f;
-                L += f * lv[j][q];
+                for (int e = 0; e < NQ; ++e) {
+                    const int off = pb + (hh * D + d0 + 4 * e) * 4;
+                    if (DPL >= 4) {
+                        ov[q][e] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kSc1));
+                    } else if (DPL == 2) {
+                        const f32x2 t2 = __builtin_bit_cast(
+                            f32x2, __builtin_amdgcn_raw_buffer_load_b64(prs, off, 0, kSc1));
+                        ov[q][e] = f32x4{t2[0], t2[1], 0.0f, 0.0f};
+                    } else {
+                        const float t1 = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, kSc1));
+                        ov[q][e] = f32x4{t1, 0.0f, 0.0f, 0.0f};
+                    }
+                }
             }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-            if (lane == 0) invL[hh] = (L > 0.0f) ? 1.0f / L : 0.0f;
+            for (int q = 0; q < CH; ++q) {
+                // splits past the last one re-read it and weigh in as nothing
+                const float ms = (c0 + q < nsplit) ? ml[q][0] : -INFINITY;
+                const float ls = ml[q][1];
+                const float Mn = fmaxf(M, ms);
+                const float Ms = (Mn == -INFINITY) ? 0.0f : Mn;
+                const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Ms);
+                const float f = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - Ms);
+                L = L * a + f * ls;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + f * ov[q][e / 4][e % 4];
+                M = Mn;
+            }
         }
-    }
-    __syncthreads();
-
-    // ---- o = sum_sp w_sp o_sp / L in split order ------------------------------------------
+        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+        __bf16* orow = reinterpret_cast<__bf16*>(out_t) + (long(b) * Hq + g * G + hh) * D + d0;
 #pragma unroll
-    for (int j = 0; j < NO; ++j) {
-        const int x = tid + 256 * j;
-        if (x >= G * D) break;
-        const int hh = x / D;
-        const int dd = x % D;
-        float o = 0.0f;
-#pragma unroll
-        for (int q = 0; q < CH; ++q)
-            if (q < nsplit) o += fw[q * G + hh] * ov[j][q];
-        for (int c0 = CH; c0 < nsplit; c0 += CH) {
-            float nv[CH];
-#pragma unroll
-            for (int q = 0; q < CH; ++q)
-                nv[q] = (c0 + q < nsplit) ? p0[(c0 + q) * stride + hh * (D + 2) + 2 + dd] : 0.0f;
-#pragma unroll
-            for (int q = 0; q < CH; ++q)
-                if (c0 + q < nsplit) o += fw[(c0 + q) * G + hh] * nv[q];
-        }
-        reinterpret_cast<__bf16*>(out_t)[(long(b) * Hq + g * G + hh) * D + dd] =
-            (__bf16)(o * invL[hh]);
+        for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(o[e] * inv);
     }
     if (INGEST) {
-        const float ws = (wk >= 0) ? c.ret_score[long(bg) * C + wk] : 0.0f;
-        __syncthreads();                              // split weights no longer read
-        ingest_finish<D>(c, bg, g, s, w, C, S, t, cnt, X, rl, u, wk, ws, false, k_t, v_t, cnn,
-                         smem, w2s, red_s, red_t, red_x);
+        // weakest of the post-step segment: over the splits' weakest entries
+        float bs = INFINITY;
+        int bt = -1, bl = -1;
+        for (int q = lane; q < nsplit; q += 64) {
+            const u32x4 wt = __builtin_amdgcn_raw_buffer_load_b128(
+                prs, q * kPart * 4 + (G * D + 2 * G) * 4, 0, kSc1);
+            const float sc = __uint_as_float(wt[0]);
+            if (weaker(sc, int(wt[1]), bs, bt)) { bs = sc; bt = int(wt[1]); bl = int(wt[2]); }
+        }
+        wave_weakest(bs, bt, bl);
+        ingest_commit<D>(c, bg, s, w, C, S, t, cnt, X, rl, u, bl, bs, r1, nk, nv);
     }
+    if (lane == 0) __hip_atomic_store(c.arrive + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -585,10 +576,10 @@ hipError_t launch_score_evict(const Shape& sh, const lte_cnn& cnn, const uint16_
                               const uint16_t* v_t, const CacheView& cache, hipStream_t st) {
     dim3 grid(unsigned(sh.B * sh.Hkv));
     if (sh.D == 128) {
-        hipLaunchKernelGGL(score_evict_kernel<128>, grid, dim3(256), 0, st, sh.s, sh.w, sh.C,
+        hipLaunchKernelGGL(score_evict_kernel<128>, grid, dim3(64), 0, st, sh.s, sh.w, sh.C,
                            sh.S, sh.Hkv, k_t, v_t, cnn, cache);
     } else {
-        hipLaunchKernelGGL(score_evict_kernel<64>, grid, dim3(256), 0, st, sh.s, sh.w, sh.C,
+        hipLaunchKernelGGL(score_evict_kernel<64>, grid, dim3(64), 0, st, sh.s, sh.w, sh.C,
                            sh.S, sh.Hkv, k_t, v_t, cnn, cache);
     }
     return hipGetLastError();
@@ -599,36 +590,29 @@ hipError_t launch_decode(const Shape& sh, bool ingest, const uint16_t* q_t, cons
                          float* part, uint16_t* out_t, hipStream_t st) {
     const int nsplit = decode_nsplit(sh);
     dim3 grid(unsigned(sh.B * sh.Hkv * nsplit));
-    dim3 fgrid(unsigned(sh.B * sh.Hkv));
     lte_cnn cn{};
     if (cnn != nullptr) cn = *cnn;
-#define LTE_FINISH(DD, GG, ING)                                                                  \
-    case GG:                                                                                     \
-        hipLaunchKernelGGL((decode_finish_kernel<DD, GG, ING>), fgrid, dim3(256), 0, st, sh.Hq, \
-                           sh.Hkv, sh.s, sh.w, sh.C, sh.S, nsplit, k_t, v_t, cn, cache, part,    \
-                           out_t);                                                               \
+#define LTE_DECODE_G(DD, GG, ING)                                                               \
+    case GG:                                                                                    \
+        hipLaunchKernelGGL((decode_step_kernel<DD, GG, ING>), grid, dim3(64), 0, st, sh.Hq,      \
+                           sh.Hkv, sh.s, sh.w, sh.C, sh.S, nsplit, q_t, k_t, v_t, cn, cache,     \
+                           part, out_t);                                                        \
         break;
-#define LTE_DECODE(DD, ING)                                                                      \
-    do {                                                                                         \
-        hipLaunchKernelGGL((decode_split_kernel<DD, ING>), grid, dim3(64), 0, st, sh.Hq, sh.Hkv, \
-                           sh.G, sh.s, sh.w, sh.C, sh.S, nsplit, q_t, k_t, v_t, cache, part);    \
-        hipError_t e_ = hipGetLastError();                                                       \
-        if (e_ != hipSuccess) return e_;                                                         \
-        switch (sh.G) {                                                                          \
-            LTE_FINISH(DD, 1, ING)                                                               \
-            LTE_FINISH(DD, 2, ING)                                                               \
-            LTE_FINISH(DD, 4, ING)                                                               \
-            LTE_FINISH(DD, 8, ING)                                                               \
-            LTE_FINISH(DD, 16, ING)                                                              \
-            default: return hipErrorInvalidValue;                                                \
-        }                                                                                        \
-    } while (0)
-    if (sh.D == 128) {
-        if (ingest) LTE_DECODE(128, true); else LTE_DECODE(128, false);
-    } else {
-        if (ingest) LTE_DECODE(64, true); else LTE_DECODE(64, false);
+#define LTE_DECODE(DD, ING)                                                                     \
+    switch (sh.G) {                                                                             \
+        LTE_DECODE_G(DD, 1, ING)                                                                \
+        LTE_DECODE_G(DD, 2, ING)                                                                \
+        LTE_DECODE_G(DD, 4, ING)                                                                \
+        LTE_DECODE_G(DD, 8, ING)                                                                \
+        LTE_DECODE_G(DD, 16, ING)                                                               \
+        default: return hipErrorInvalidValue;                                                   \
     }
-#undef LTE_FINISH
+    if (sh.D == 128) {
+        if (ingest) { LTE_DECODE(128, true) } else { LTE_DECODE(128, false) }
+    } else {
+        if (ingest) { LTE_DECODE(64, true) } else { LTE_DECODE(64, false) }
+    }
+#undef LTE_DECODE_G
 #undef LTE_DECODE
     return hipGetLastError();
 }

@@ -63,6 +63,7 @@ inline lte_cache_layout cache_layout(const Shape& sh) {
     L.weak = off; off = align256(off + bg * 4);
     L.nx_slot = off; off = align256(off + bg * 4);
     L.nx_score = off; off = align256(off + bg * 4);
+    L.arrive = off; off = align256(off + bg * 4);
     L.total = off;
     return L;
 }
@@ -81,6 +82,7 @@ struct CacheView {
     int32_t* weak;         // [B][Hkv] weakest slot of a full segment, else -1
     int32_t* nx_slot;      // [B][Hkv] decision for the next leaving token
     float* nx_score;       // [B][Hkv] its score
+    int32_t* arrive;       // [B][Hkv] decode split arrivals, 0 between calls
 };
 
 inline CacheView cache_view(const Shape& sh, void* base) {
@@ -99,6 +101,7 @@ inline CacheView cache_view(const Shape& sh, void* base) {
     c.weak = reinterpret_cast<int32_t*>(p + L.weak);
     c.nx_slot = reinterpret_cast<int32_t*>(p + L.nx_slot);
     c.nx_score = reinterpret_cast<float*>(p + L.nx_score);
+    c.arrive = reinterpret_cast<int32_t*>(p + L.arrive);
     return c;
 }
 
@@ -126,6 +129,11 @@ inline size_t select_scratch_words(int64_t T) {
 // Decode split-K: cache slots per workgroup and the number of splits.
 constexpr int kDecodeSplitKeys = 64;
 inline int decode_nsplit(const Shape& sh) { return (sh.S + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
+// Floats per split partial: o [G][D], then (max, sum) per head and the split's
+// weakest segment entry (score, token, slot), padded to 16 bytes.
+__host__ __device__ constexpr int decode_part_floats(int G, int D) {
+    return G * D + ((2 * G + 3 + 3) & ~3);
+}
 
 struct WsLayout {
     size_t scores, rank, thr, ncand, w1p, select_scratch, dec_part, total;
@@ -137,7 +145,7 @@ inline WsLayout ws_layout(const Shape& sh, int64_t T) {
     size_t bg = size_t(sh.B) * sh.Hkv;
     size_t off = 0;
     W.dec_part = off;
-    off = align256(off + bg * size_t(decode_nsplit(sh)) * sh.G * (sh.D + 2) * 4);
+    off = align256(off + bg * size_t(decode_nsplit(sh)) * decode_part_floats(sh.G, sh.D) * 4);
     W.scores = off; off = align256(off + bg * size_t(T) * 4);
     W.rank = off; off = align256(off + bg * size_t(T) * 4);
     W.thr = off; off = align256(off + bg * size_t(T) * 4);

@@ -7,8 +7,8 @@
 // token is computable once its receptive field (tokens j-2 .. j+2 for two
 // kernel-3 layers) is present.
 //
-// Per call: one workgroup of 256 threads (4 waves) scores the 124 tokens
-// [t0, t0+124).  Layer 1 is written as Y_tap = W1[:, :, tap] . x per token
+// score_chunk: one workgroup of 256 threads (4 waves) scores the 124 tokens
+// [t0, t0+124) (prefill).  score_wave: one wave scores 28 tokens (decode).  Layer 1 is written as Y_tap = W1[:, :, tap] . x per token
 // (v_mfma_f32_32x32x16_bf16, 32 tokens x 96 outputs per wave), then
 // h[j] = b1 + Y_0[j-1] + Y_1[j] + Y_2[j+1].
 #pragma once
@@ -132,6 +132,90 @@ __device__ __forceinline__ void score_chunk(unsigned char* buf, const float* w2s
         }
     }
     __syncthreads();
+}
+
+// One wave scores tokens [t0, t0+28) clipped to [tlo, thi] (the decode
+// path's deferred batches, split across the waves of a step).  Same
+// arithmetic per token as score_chunk: layer 1 on v_mfma_f32_32x32x16_bf16
+// over the 32 rows t0-2 .. t0+29, with W1's bf16 operands built from the fp32
+// weights; a token's score does not depend on how tokens are grouped.
+//   Y        LDS of kWaveScoreBytes, wave-private
+//   w1g      fp32 W1 of this head [hidden][2D][3]; w2g [hidden][3]
+constexpr int kWaveScoreTile = 28;
+constexpr int kWaveScoreBytes = 32 * 96 * 4;
+
+template <int D, class XRow, class AZero, class Store>
+__device__ __forceinline__ void score_wave(float* Y, const float* __restrict__ w1g,
+                                           const float* __restrict__ b1g,
+                                           const float* __restrict__ w2g, float b2g, int t0,
+                                           int tlo, int thi, XRow x_row, AZero a_zero,
+                                           Store store) {
+    constexpr int KK = ScoreSmem<D>::KK;
+    const int lane = threadIdx.x & 63;
+    const int tok = t0 - 2 + (lane & 31);
+    const uint16_t* kp = nullptr;
+    const uint16_t* vp = nullptr;
+    const bool ok = x_row(tok, kp, vp);
+    // B operand of (tap, kk): element e of lane l is W1[o = l % 32][c = 16 kk + 8 (l/32) + e][tap];
+    // one tap at a time (a rare path: registers matter more than reloads)
+    const float* wrow = w1g + ((lane & 31) * (2 * D) + (lane >> 5) * 8) * 3;
+    for (int tp = 0; tp < 3; ++tp) {
+        f32x16 acc = f32x16{};
+#pragma unroll 2
+        for (int kk = 0; kk < KK; ++kk) {
+            const int c = kk * 16 + (lane >> 5) * 8;
+            bf16x8 a = bf16x8{};
+            if (ok) a = *reinterpret_cast<const bf16x8*>((c < D) ? (kp + c) : (vp + (c - D)));
+            bf16x8 bw;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bw[e] = (__bf16)wrow[(kk * 16 + e) * 3 + tp];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw, acc, 0, 0, 0);
+        }
+        // accumulator element e of lane l: row 8 (e/4) + 4 (l/32) + e%4, column l % 32
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+            Y[row * 96 + tp * 32 + (lane & 31)] = acc[e];
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // hidden layer for rows 1..30 (tokens t0-1 .. t0+28); GELU(h) of row r
+    // overwrites Y_1 of row r, which no other lane reads
+    for (int x = lane; x < 30 * kHidden; x += 64) {
+        const int r = x / kHidden + 1;
+        const int o = x % kHidden;
+        const int t = t0 - 2 + r;
+        float a = 0.0f;
+        if (!a_zero(t)) {
+            const float h = b1g[o] + Y[(r - 1) * 96 + o] + Y[r * 96 + 32 + o] +
+                            Y[(r + 1) * 96 + 64 + o];
+            a = gelu_erf(h);
+        }
+        Y[r * 96 + 32 + o] = a;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // output layer + sigmoid for tokens t0 .. t0+27 (rows 2 .. 29)
+    if (lane < kWaveScoreTile) {
+        const int t = t0 + lane;
+        if (t >= tlo && t <= thi) {
+            float z = b2g;
+            const float* a = Y + 32;
+            const int r = lane + 2;
+#pragma unroll 8
+            for (int o = 0; o < kHidden; ++o) {
+                z += w2g[o * 3 + 0] * a[(r - 1) * 96 + o] + w2g[o * 3 + 1] * a[r * 96 + o] +
+                     w2g[o * 3 + 2] * a[(r + 1) * 96 + o];
+            }
+            store(t, 1.0f / (1.0f + expf(-z)));
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace lte

@@ -42,7 +42,7 @@ class _CNN(ctypes.Structure):
 class _CacheLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("k", "v", "ret_idx", "ret_score", "ring_score", "count", "pos",
-                 "next_unscored", "flags", "weak", "nx_slot", "nx_score", "total")]
+                 "next_unscored", "flags", "weak", "nx_slot", "nx_score", "arrive", "total")]
 
 
 class _WsLayout(ctypes.Structure):
@@ -297,6 +297,7 @@ class Layer:
             "weak": view("weak", bg, torch.int32, (c.batch, c.kv_heads)),
             "nx_slot": view("nx_slot", bg, torch.int32, (c.batch, c.kv_heads)),
             "nx_score": view("nx_score", bg, torch.float32, (c.batch, c.kv_heads)),
+            "arrive": view("arrive", bg, torch.int32, (c.batch, c.kv_heads)),
         }
 
     def cache_export(self, cache) -> dict:

@@ -100,7 +100,7 @@ def test_cache_layout_matches_the_documented_sections():
              ("ret_idx", bg * c.capacity * 4), ("ret_score", bg * c.capacity * 4),
              ("ring_score", bg * c.window * 4), ("count", bg * 4), ("pos", bg * 8),
              ("next_unscored", bg * 8), ("flags", bg * 4), ("weak", bg * 4),
-             ("nx_slot", bg * 4), ("nx_score", bg * 4)]
+             ("nx_slot", bg * 4), ("nx_score", bg * 4), ("arrive", bg * 4)]
     off = 0
     for name, n in sizes:
         assert L[name] == off, name
