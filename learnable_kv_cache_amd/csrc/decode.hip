@@ -51,7 +51,8 @@ namespace lte {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int KPB = kDecodeSplitKeys;          // cache slots per wave (64)
+constexpr int KPB = 64;                        // cache slots per wave
+constexpr int NWV = kDecodeSplitKeys / KPB;    // waves per workgroup (2)
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]
 // and D[4(l/16)+r][l%16].
@@ -227,7 +228,8 @@ __global__ __launch_bounds__(64) void score_evict_kernel(int s, int w, int C, in
 
 // One decode step (INGEST) or an attention over the cache as it is.
 template <int D, int G, bool INGEST>
-__global__ __launch_bounds__(64, 3) void decode_step_kernel(
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_step_kernel(
     int Hq, int Hkv, int s, int w, int C, int S, int nsplit,
     const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
     const uint16_t* __restrict__ v_t, lte_cnn cnn, CacheView c, float* __restrict__ part,
@@ -237,16 +239,21 @@ __global__ __launch_bounds__(64, 3) void decode_step_kernel(
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int kVBytes = KPB * CPR * 16;
     constexpr int kBuf = kVBytes > kWaveScoreBytes ? kVBytes : kWaveScoreBytes;
-    __shared__ __align__(16) u32x4 Vs[kBuf / 16];     // V tile; later the scorer's rows
+    // per wave: its V tile; later its scorer rows (and wave 1's partial for wave 0,
+    // then the last-arrival flag).  32 KB: five workgroups fit a CU.
+    __shared__ __align__(16) u32x4 Vs[NWV][kBuf / 16];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int q16 = lane >> 4;
     const int sp = blockIdx.x % nsplit;
     const int bg = blockIdx.x / nsplit;
     const int b = bg / Hkv;
     const int g = bg % Hkv;
-    const int slot0 = sp * KPB;
+    const int slot0 = (sp * NWV + wave) * KPB;
+    u32x4* Vw = Vs[wave];
     const long base = long(bg) * S * D;
 
     // ---- bulk loads first: the V tile (direct to LDS), q (B operand) and the K
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(64, 3) void decode_step_kernel(
         const int gch = (cidx % CPR) ^ vswz<D>(row);
         const uint16_t* src = c.v + base + long(min(slot0 + row, S - 1)) * D + gch * 8;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(&Vs[64 * x]),
+                                         (__attribute__((address_space(3))) void*)(&Vw[64 * x]),
                                          16, 0, 0);
     }
     bf16x8 qf[KS];
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(64, 3) void decode_step_kernel(
             if (fs[f] < 0 || kk < 0 || kk >= KPB || fs[f] >= S) continue;
             const uint16_t* rv = (f == 1) ? c.v + base + long(s + C + tslot) * D : v_t + long(bg) * D;
             if (lane < CPR)
-                Vs[kk * CPR + lane] = *reinterpret_cast<const u32x4*>(rv + 8 * (lane ^ vswz<D>(kk)));
+                Vw[kk * CPR + lane] = *reinterpret_cast<const u32x4*>(rv + 8 * (lane ^ vswz<D>(kk)));
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -438,7 +445,7 @@ __global__ __launch_bounds__(64, 3) void decode_step_kernel(
                 const int key = 32 * cc + 16 * r2 + 4 * q16 + (l16 >> 2);
                 const int d0 = 16 * dt + 4 * (l16 & 3);
                 const __bf16* src = reinterpret_cast<const __bf16*>(
-                                        &Vs[key * CPR + ((d0 >> 3) ^ vswz<D>(key))]) + (d0 & 7);
+                                        &Vw[key * CPR + ((d0 >> 3) ^ vswz<D>(key))]) + (d0 & 7);
                 const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) v4i16*)(src));
                 const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
@@ -449,62 +456,97 @@ __global__ __launch_bounds__(64, 3) void decode_step_kernel(
             oacc[dt] = mfma16(a, pl[cc], oacc[dt]);
         }
     }
-    // partial of this split: o [G][D] at 0, (max, sum) of head h at G*D + 2h
+    // ---- the waves' partials combine into one per workgroup: o [G][D] at 0, (max, sum)
+    //      of head h at G*D + 2h, the weakest segment entry at G*D + 2G -----------------
     constexpr int kPart = decode_part_floats(G, D);             // floats per split
     __amdgpu_buffer_rsrc_t prs = part_rsrc(part + long(bg) * nsplit * kPart);
-    if (l16 < G) {
-        const int pbase = sp * kPart * 4;                          // bytes
+    if (INGEST) wave_weakest(wsc, wtk, wsl);
+    float* xw = reinterpret_cast<float*>(Vs[1]);               // wave 1's, read by now
+    if (wave == 1) {
+        if (l16 < G) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const f32x4 o4 = oacc[dt];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), prs,
-                                                   pbase + (l16 * D + 16 * dt + 4 * q16) * 4, 0,
-                                                   kSc1);
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4*>(&xw[l16 * D + 16 * dt + 4 * q16]) = oacc[dt];
+            if (q16 == 0) *reinterpret_cast<f32x2*>(&xw[G * D + 2 * l16]) = f32x2{m, l};
         }
-        if (q16 == 0) {
-            const f32x2 ml = {m, l};
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), prs,
-                                                  pbase + (G * D + 2 * l16) * 4, 0, kSc1);
-        }
+        if (INGEST && lane == 0)
+            *reinterpret_cast<u32x4*>(&xw[G * D + 2 * G]) =
+                u32x4{__float_as_uint(wsc), uint32_t(wtk), uint32_t(wsl), 0u};
     }
-    if (INGEST) {
-        wave_weakest(wsc, wtk, wsl);
-        if (lane == 0) {
+    __syncthreads();
+    if (wave == 0) {
+        const int pbase = sp * kPart * 4;                          // bytes
+        if (l16 < G) {
+            const f32x2 ml1 = *reinterpret_cast<const f32x2*>(&xw[G * D + 2 * l16]);
+            const float Mn = fmaxf(m, ml1[0]);
+            const float Ms = (Mn == -INFINITY) ? 0.0f : Mn;
+            const float a0 = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - Ms);
+            const float a1 = (ml1[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml1[0] - Ms);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xw[l16 * D + 16 * dt + 4 * q16]);
+                const f32x4 o4 = oacc[dt] * a0 + o1 * a1;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), prs,
+                                                       pbase + (l16 * D + 16 * dt + 4 * q16) * 4,
+                                                       0, kSc1);
+            }
+            if (q16 == 0) {
+                const f32x2 ml = {Mn, l * a0 + ml1[1] * a1};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), prs,
+                                                      pbase + (G * D + 2 * l16) * 4, 0, kSc1);
+            }
+        }
+        if (INGEST && lane == 0) {
+            const u32x4 w1 = *reinterpret_cast<const u32x4*>(&xw[G * D + 2 * G]);
+            if (weaker(__uint_as_float(w1[0]), int(w1[1]), wsc, wtk)) {
+                wsc = __uint_as_float(w1[0]);
+                wtk = int(w1[1]);
+                wsl = int(w1[2]);
+            }
             const u32x4 wt = {__float_as_uint(wsc), uint32_t(wtk), uint32_t(wsl), 0u};
-            __builtin_amdgcn_raw_buffer_store_b128(wt, prs, sp * kPart * 4 + (G * D + 2 * G) * 4,
-                                                   0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b128(wt, prs, pbase + (G * D + 2 * G) * 4, 0, kSc1);
         }
     }
 
     // ---- this step's share of the deferred batch ---------------------------------------
-    if (INGEST) {
-        if (t == u + w - 3) {
-            float* Y = reinterpret_cast<float*>(Vs);
-            const int nch = (t - 1 - u + kWaveScoreTile - 1) / kWaveScoreTile;
-            for (int ch = sp; ch < nch; ch += nsplit)
-                score_deferred_chunk<D>(c, bg, g, s, w, C, S, t, u, ch, k_t, v_t, cnn, Y);
-        }
+    if (INGEST && t == u + w - 3) {
+        __syncthreads();                          // wave 1's partial read: its rows are free
+        float* Y = reinterpret_cast<float*>(Vw);
+        const int nch = (t - 1 - u + kWaveScoreTile - 1) / kWaveScoreTile;
+        for (int ch = sp * NWV + wave; ch < nch; ch += nsplit * NWV)
+            score_deferred_chunk<D>(c, bg, g, s, w, C, S, t, u, ch, k_t, v_t, cnn, Y);
     }
 
-    // ---- arrival: the last wave of (b, g) merges and finishes the step --------------------
+    // ---- arrival: the last workgroup of (b, g) merges and finishes the step ---------------
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);            // partials (and row copies) complete
+    __builtin_amdgcn_s_waitcnt(0);            // partials, row copies, scores complete
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    int old = 0;
-    if (lane == 0)
-        old = __hip_atomic_fetch_add(c.arrive + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old != nsplit - 1) return;
+    __syncthreads();
+    int* last_arrival = reinterpret_cast<int*>(Vs[1]);        // every LDS use is over
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(c.arrive + bg, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        *last_arrival = (old == nsplit - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    if (*last_arrival == 0) return;
 
-    // merge: lane handles head hh = lane / LPH, dims [d0, d0 + DPL), online over the
+    // the splits' weakest segment entries, loaded alongside the first merge round
+    u32x4 wt0 = u32x4{__float_as_uint(INFINITY), ~0u, ~0u, 0u};
+    if (INGEST && wave == 0 && lane < nsplit)
+        wt0 = __builtin_amdgcn_raw_buffer_load_b128(prs, lane * kPart * 4 + (G * D + 2 * G) * 4,
+                                                    0, kSc1);
+    // merge: thread handles head hh = tid / TPH, dims [d0, d0 + DPL), online over the
     // splits in split order; coherent loads CH splits at a time
     {
-        constexpr int LPH = 64 / G;               // lanes per head
-        constexpr int DPL = D / LPH;              // dims per lane: 1, 2 or a multiple of 4
+        constexpr int NT = 64 * NWV;
+        constexpr int TPH = (G * D >= NT ? NT : G * D) / G;      // threads per head
+        constexpr int DPL = D / TPH;              // dims per thread: 1, 2 or a multiple of 4
         constexpr int NQ = DPL >= 4 ? DPL / 4 : 1;        // loads of o per split
         constexpr int CH = 96 / (DPL + 2) > 0 ? 96 / (DPL + 2) : 1;   // splits per round
-        const int hh = lane / LPH;
-        const int d0 = (lane % LPH) * DPL;
+        const bool active = tid < TPH * G;
+        const int hh = active ? tid / TPH : 0;
+        const int d0 = active ? (tid % TPH) * DPL : 0;
         float M = -INFINITY, L = 0.0f;
         float o[DPL];
 #pragma unroll
@@ -551,14 +593,16 @@ __global__ __launch_bounds__(64, 3) void decode_step_kernel(
         }
         const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
         __bf16* orow = reinterpret_cast<__bf16*>(out_t) + (long(b) * Hq + g * G + hh) * D + d0;
+        if (active) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(o[e] * inv);
+            for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(o[e] * inv);
+        }
     }
-    if (INGEST) {
+    if (INGEST && wave == 0) {
         // weakest of the post-step segment: over the splits' weakest entries
-        float bs = INFINITY;
-        int bt = -1, bl = -1;
-        for (int q = lane; q < nsplit; q += 64) {
+        float bs = __uint_as_float(wt0[0]);
+        int bt = int(wt0[1]), bl = int(wt0[2]);
+        for (int q = lane + 64; q < nsplit; q += 64) {
             const u32x4 wt = __builtin_amdgcn_raw_buffer_load_b128(
                 prs, q * kPart * 4 + (G * D + 2 * G) * 4, 0, kSc1);
             const float sc = __uint_as_float(wt[0]);
@@ -567,7 +611,7 @@ __global__ __launch_bounds__(64, 3) void decode_step_kernel(
         wave_weakest(bs, bt, bl);
         ingest_commit<D>(c, bg, s, w, C, S, t, cnt, X, rl, u, bl, bs, r1, nk, nv);
     }
-    if (lane == 0) __hip_atomic_store(c.arrive + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(c.arrive + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -594,9 +638,9 @@ hipError_t launch_decode(const Shape& sh, bool ingest, const uint16_t* q_t, cons
     if (cnn != nullptr) cn = *cnn;
 #define LTE_DECODE_G(DD, GG, ING)                                                               \
     case GG:                                                                                    \
-        hipLaunchKernelGGL((decode_step_kernel<DD, GG, ING>), grid, dim3(64), 0, st, sh.Hq,      \
-                           sh.Hkv, sh.s, sh.w, sh.C, sh.S, nsplit, q_t, k_t, v_t, cn, cache,     \
-                           part, out_t);                                                        \
+        hipLaunchKernelGGL((decode_step_kernel<DD, GG, ING>), grid, dim3(64 * NWV), 0, st,       \
+                           sh.Hq, sh.Hkv, sh.s, sh.w, sh.C, sh.S, nsplit, q_t, k_t, v_t, cn,     \
+                           cache, part, out_t);                                                 \
         break;
 #define LTE_DECODE(DD, ING)                                                                     \
     switch (sh.G) {                                                                             \

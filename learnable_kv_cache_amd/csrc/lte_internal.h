@@ -126,8 +126,8 @@ inline size_t select_scratch_words(int64_t T) {
     return size_t(4 * Tp) + align256(size_t(2 * select_nsnap_max(T) * select_words(T)) * 4) / 4;
 }
 
-// Decode split-K: cache slots per workgroup and the number of splits.
-constexpr int kDecodeSplitKeys = 64;
+// Decode split-K: cache slots per workgroup (two waves of 64) and the number of splits.
+constexpr int kDecodeSplitKeys = 128;
 inline int decode_nsplit(const Shape& sh) { return (sh.S + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
 // Floats per split partial: o [G][D], then (max, sum) per head and the split's
 // weakest segment entry (score, token, slot), padded to 16 bytes.
