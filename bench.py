@@ -13,7 +13,7 @@ each with the roofline of its dominant kernel, next to the CPU oracle timed on
 this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
-                       [--no-cpu-baseline] [--no-decode]
+                       [--no-cpu-baseline] [--no-decode] [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -48,7 +48,22 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="sequences the oracle runs for the CPU baseline (0: one per core)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """Five device-to-device copies of a known size: the reference dispatches that
+    scale the FETCH_SIZE / WRITE_SIZE counters of a profiled kernel to bytes."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "copies": 5}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -178,6 +193,10 @@ def main():
               "(batch and KV-head sharding need no communication and are described in the "
               "design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     from learnable_kv_cache_amd import lte, synth
@@ -344,7 +363,9 @@ def main():
             "roofline": {"bound": "hbm", "achieved": achieved_b / 1e9,
                          "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                          "frac": achieved_b / PEAK_HBM_BPS, "bytes_per_step": step_bytes,
-                         "traffic": None},
+                         "traffic": measured_traffic(
+                             "decode_step", os.path.join(ROOT, "learnable_kv_cache_amd", "csrc",
+                                                         "decode.hip"))},
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, T, args.cpu_sample)
