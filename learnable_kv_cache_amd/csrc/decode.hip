@@ -25,34 +25,35 @@
 // so whoever finishes an ingest (or builds the cache) also records the next
 // one (nx_slot, nx_score): the attention of a step never waits for it.
 //
-// A decode step is one launch of one-wave workgroups, one per 64 cache
-// slots of a (batch, KV head):
-//   * each reads its slots in the PRE-step state with the post-ingest
-//     contents substituted: ring slot t mod w (and sink slot t) come from the
-//     k_t/v_t inputs, and the segment slot the leaving token takes reads that
-//     token from its ring slot (that wave also copies the row into the slot:
-//     no other wave reads it).  K rows go straight into MFMA operand
-//     registers; V rows are loaded into LDS by direct global->LDS loads and
-//     read back transposed (ds_read_b64_tr_b16).  q.k and p.v run on
-//     v_mfma_f32_16x16x32_bf16 with the G <= 16 query heads of the KV head
-//     as the 16 columns;
-//   * on a scoring step the waves of a (batch, KV head) share the deferred
-//     batch, 28 tokens per wave call;
-//   * each wave writes (max, sum, unnormalised o) per head with device-scope
-//     coherent stores and counts itself in on the (batch, KV head)'s arrival
-//     word; the last to arrive merges the partials in split order
-//     (deterministic), writes o_t, applies the rest of the ingest, records
-//     the next decision and clears the arrival word.  The partials bypass
-//     the non-coherent L2 copies instead of a cache-wide write-back and
-//     invalidate, which a device-scope fence would cost on gfx950.
+// A decode step is one launch.  Each (batch, KV head) is served by one
+// workgroup of 8 waves, or, when there are fewer than 128 such pairs, by a few
+// workgroups that split its visible rows:
+//   * the visible rows (sink, post-step segment, window) are read in chunks of
+//     32 by direct global->LDS loads of whole 256-byte rows, so only occupied
+//     slots cost bandwidth.  Rows that differ in the post-ingest state are
+//     read from where they are before the step: the new token from the k_t/v_t
+//     inputs, the leaving token (taking segment slot X) from its ring slot;
+//   * q.k and p.v run on v_mfma_f32_16x16x32_bf16 with the G <= 16 query heads
+//     of the KV head as the 16 columns; V is read back transposed
+//     (ds_read_b64_tr_b16);
+//   * the waves' (max, sum, unnormalised o) merge in LDS, in wave order.  With
+//     several workgroups per pair, each writes its partial with device-scope
+//     coherent stores and counts itself in on the pair's arrival word; the last
+//     to arrive merges the partials in split order (deterministic);
+//   * the finishing workgroup writes o_t, moves the leaving token's row into its
+//     segment slot, writes k_t/v_t into the ring, records the next decision and
+//     the weakest segment entry (computed by every workgroup while its first
+//     chunks load);
+//   * on a scoring step the waves share the deferred batch, 28 tokens per wave
+//     call.
+// The partials bypass the non-coherent L2 copies instead of a cache-wide
+// write-back and invalidate, which a device-scope fence would cost on gfx950.
 #include "score_core.h"
 
 namespace lte {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int KPB = 64;                        // cache slots per wave
-constexpr int NWV = kDecodeSplitKeys / KPB;    // waves per workgroup (2)
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]
 // and D[4(l/16)+r][l%16].
@@ -98,12 +99,12 @@ __device__ void score_deferred_chunk(const CacheView& c, int bg, int g, int s, i
                                      int S, int t, int u, int ch,
                                      const uint16_t* __restrict__ k_t,
                                      const uint16_t* __restrict__ v_t, const lte_cnn& cnn,
-                                     float* Y) {
+                                     float* Ya, float* Yb) {
     const uint16_t* kring = c.k + (long(bg) * S + s + C) * D;
     const uint16_t* vring = c.v + (long(bg) * S + s + C) * D;
     float* rs = c.ring_score + long(bg) * w;
     score_wave<D>(
-        Y, cnn.w1 + long(g) * kHidden * 2 * D * 3, cnn.b1 + g * kHidden,
+        Ya, Yb, cnn.w1 + long(g) * kHidden * 2 * D * 3, cnn.b1 + g * kHidden,
         cnn.w2 + g * kHidden * 3, cnn.b2[g], u + kWaveScoreTile * ch, u, t - 2,
         [&](int x, const uint16_t*& kp, const uint16_t*& vp) {
             if (x < 0 || x > t) return false;
@@ -184,7 +185,8 @@ __global__ __launch_bounds__(64) void score_evict_kernel(int s, int w, int C, in
                                                          const uint16_t* __restrict__ k_t,
                                                          const uint16_t* __restrict__ v_t,
                                                          lte_cnn cnn, CacheView c) {
-    __shared__ __align__(16) float Y[kWaveScoreBytes / 4];
+    __shared__ __align__(16) float Ya[kWaveScoreBytesA / 4];
+    __shared__ __align__(16) float Yb[kWaveScoreBytesB / 4];
     const int lane = threadIdx.x;
     const int bg = blockIdx.x;
     const int t = int(c.pos[bg]);
@@ -220,54 +222,146 @@ __global__ __launch_bounds__(64) void score_evict_kernel(int s, int w, int C, in
     if (t == u + w - 3) {                     // deferred batch: ring rows of tokens < t
         const int nch = (t - 1 - u + kWaveScoreTile - 1) / kWaveScoreTile;
         for (int ch = 0; ch < nch; ++ch)
-            score_deferred_chunk<D>(c, bg, bg % Hkv, s, w, C, S, t, u, ch, k_t, v_t, cnn, Y);
+            score_deferred_chunk<D>(c, bg, bg % Hkv, s, w, C, S, t, u, ch, k_t, v_t, cnn, Ya, Yb);
     }
     __builtin_amdgcn_s_waitcnt(0);            // ring row copied before it is overwritten
     ingest_commit<D>(c, bg, s, w, C, S, t, cnt, X, rl, u, wsl, wsc, r1, nk, nv);
 }
 
+// Per-wave LDS of the decode step: one chunk of 32 visible rows of K (in Ks) and
+// of V (in Vs), each a [32][D/8] array of 16-byte pieces; afterwards the wave's
+// scorer rows (taps 0-1 in Ks, tap 2 in Vs) and its partial output.  K and V
+// tiles are separate LDS objects so that the compiler can tell a tile being
+// read from one being filled by direct loads, and does not wait for the latter.
+template <int D>
+struct DecTile {
+    static constexpr int CPR = D / 8;                      // 16-byte pieces per row
+    static constexpr int kRows = 32;                       // rows per chunk
+    static constexpr int kTile = kRows * CPR;              // pieces per tensor tile
+    static constexpr int kLoads = kTile / 64;              // direct loads per tensor tile
+    static constexpr int kKW = (kTile * 16 > kWaveScoreBytesA ? kTile * 16 : kWaveScoreBytesA) / 16;
+    static constexpr int kVW = (kTile * 16 > kWaveScoreBytesB ? kTile * 16 : kWaveScoreBytesB) / 16;
+};
+
+// LDS piece swizzle of K tile row r: logical piece c of row r sits at c ^ kswz(r).
+// The q.k operand read takes one piece of 16 consecutive rows per 16 lanes; the
+// swizzle spreads them over 256 bytes of banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+
 // One decode step (INGEST) or an attention over the cache as it is.
+//
+// The slots of (b, g) are read in chunks of 32 rows in a fixed list: the ring
+// chunks first (slots s+C .. s+C+w-1, which need no state to address), then the
+// chunks of [0, s+C) that hold a sink token or a segment entry -- an empty
+// segment costs nothing.  With one workgroup per (b, g) the list is dealt
+// round-robin to the 8 waves; with nsplit > 1 each workgroup takes a contiguous
+// run of it.  Rows past a chunk's valid ones re-read a valid row.  The list, the
+// order and the split depend only on the visible set, so the fused step and
+// score_evict + attend produce identical bits.
+//
+// A chunk's K and V rows arrive by direct global->LDS loads of whole 256-byte
+// rows, issued as soon as the wave's tiles are free.  Loads whose results are only
+// needed by the ingest (segment scores, the leaving token's row, the next leaving
+// token's score) are issued before the chunks are computed, so the ingest at the
+// end only stores.
 template <int D, int G, bool INGEST>
-__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(3)))
-void decode_step_kernel(
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     int Hq, int Hkv, int s, int w, int C, int S, int nsplit,
     const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
     const uint16_t* __restrict__ v_t, lte_cnn cnn, CacheView c, float* __restrict__ part,
     uint16_t* __restrict__ out_t) {
+    using TL = DecTile<D>;
+    constexpr int NW = kDecodeWaves;
+    constexpr int RW = TL::kRows;
+    constexpr int NL = TL::kLoads;
     constexpr int KS = D / 32;                 // q.k k-steps
     constexpr int DT = D / 16;                 // p.v output tiles
-    constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int kVBytes = KPB * CPR * 16;
-    constexpr int kBuf = kVBytes > kWaveScoreBytes ? kVBytes : kWaveScoreBytes;
-    // per wave: its V tile; later its scorer rows (and wave 1's partial for wave 0,
-    // then the last-arrival flag).  32 KB: five workgroups fit a CU.
-    __shared__ __align__(16) u32x4 Vs[NWV][kBuf / 16];
+    constexpr int CPR = TL::CPR;
+    constexpr int PW = decode_part_floats(G, D);
+    constexpr int kScan = kMaxCapacity / (64 * NW);     // segment entries per thread
+    static_assert(G * D * 4 <= TL::kKW * 16 && 2 * G * 4 <= TL::kVW * 16, "wave partials fit");
+    __shared__ __align__(16) u32x4 Ks[NW][TL::kKW];
+    __shared__ __align__(16) u32x4 Vs[NW][TL::kVW];
+    __shared__ float wk_sc[NW];
+    __shared__ int wk_tk[NW], wk_sl[NW];
+    __shared__ int last_flag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int q16 = lane >> 4;
     const int sp = blockIdx.x % nsplit;
     const int bg = blockIdx.x / nsplit;
     const int b = bg / Hkv;
     const int g = bg % Hkv;
-    const int slot0 = (sp * NWV + wave) * KPB;
-    u32x4* Vw = Vs[wave];
+    u32x4* Kt = Ks[wave];
+    u32x4* Vt = Vs[wave];
     const long base = long(bg) * S * D;
+    const char* kb = reinterpret_cast<const char*>(c.k + base);
+    const char* vb = reinterpret_cast<const char*>(c.v + base);
 
-    // ---- bulk loads first: the V tile (direct to LDS), q (B operand) and the K
-    //      rows (A operands of q.k), in the pre-step state -------------------------------
+    // list entries [e_lo, e_lo + per) of this workgroup: nr ring chunks, then head chunks
+    const int nr = (w + RW - 1) / RW;
+    const int nh = (s + C + RW - 1) / RW;
+    const int per = nsplit > 1 ? (nr + nh + nsplit - 1) / nsplit : nr + nh;
+    const int e_lo = sp * per;
+    const int ent0 = e_lo + wave;
+
+    // A tile piece x*64 + lane is row (x*64+lane)/CPR at position (x*64+lane)%CPR and
+    // holds that row's logical piece position ^ swizzle(row); rows are byte offsets
+    // from this (b, g)'s K and V slots.
+    auto kaddr = [&](const uint32_t (&roff)[NL], int x) {
+        const int pidx = 64 * x + lane;
+        return kb + roff[x] + 16 * ((pidx % CPR) ^ kswz<D>(pidx / CPR));
+    };
+    auto vaddr = [&](const uint32_t (&roff)[NL], int x) {
+        const int pidx = 64 * x + lane;
+        return vb + roff[x] + 16 * ((pidx % CPR) ^ vswz<D>(pidx / CPR));
+    };
+    auto load_lds = [&](const uint32_t (&roff)[NL]) {
 #pragma unroll
-    for (int x = 0; x < CPR; ++x) {
-        const int cidx = 64 * x + lane;
-        const int row = cidx / CPR;
-        const int gch = (cidx % CPR) ^ vswz<D>(row);
-        const uint16_t* src = c.v + base + long(min(slot0 + row, S - 1)) * D + gch * 8;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(&Vw[64 * x]),
-                                         16, 0, 0);
+        for (int x = 0; x < NL; ++x) {
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)kaddr(roff, x),
+                (__attribute__((address_space(3))) void*)(&Kt[64 * x]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)vaddr(roff, x),
+                (__attribute__((address_space(3))) void*)(&Vt[64 * x]), 16, 0, 0);
+        }
+    };
+    // ring chunk i: slots s+C+32i .. (rows past the ring re-read its last slot)
+    auto ring_rows = [&](int i, uint32_t (&roff)[NL]) {
+        const int r0 = RW * i + lane / CPR;
+#pragma unroll
+        for (int x = 0; x < NL; ++x)
+            roff[x] = uint32_t(s + C + min(r0 + x * (64 / CPR), w - 1)) * (D * 2);
+    };
+
+    // ring chunks can be requested before the state is known
+    const bool early0 = ent0 < nr && ent0 < e_lo + per;
+    if (early0) {
+        uint32_t roff[NL];
+        ring_rows(ent0, roff);
+        load_lds(roff);
     }
+    // the segment's scores and tokens, for the weakest entry after the ingest
+    float sc_e[kScan];
+    int tk_e[kScan];
+    if (INGEST) {
+#pragma unroll
+        for (int i = 0; i < kScan; ++i) {
+            const int e = tid + i * 64 * NW;
+            sc_e[i] = INFINITY;
+            tk_e[i] = -1;
+            if (e < C) {
+                sc_e[i] = c.ret_score[long(bg) * C + e];
+                tk_e[i] = c.ret_idx[long(bg) * C + e];
+            }
+        }
+    }
+    // q: B operand of q.k, head l16 (zero past G), dims 32kk + 8q16 .. +7
     bf16x8 qf[KS];
     {
         const bool hv = l16 < G;
@@ -276,16 +370,14 @@ void decode_step_kernel(
         for (int kk = 0; kk < KS; ++kk)
             qf[kk] = hv ? *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * q16) : bf16x8{};
     }
-    bf16x8 ka[4][KS];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const uint16_t* r = c.k + base + long(min(slot0 + 16 * mt + l16, S - 1)) * D;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            ka[mt][kk] = *reinterpret_cast<const bf16x8*>(r + 32 * kk + 8 * q16);
+    // the new token's row pieces (lanes < D/8): the LDS patches and the ingest
+    u32x4 nk = u32x4{}, nvv = u32x4{};
+    if (INGEST && lane < CPR) {
+        nk = *reinterpret_cast<const u32x4*>(k_t + long(bg) * D + lane * 8);
+        nvv = *reinterpret_cast<const u32x4*>(v_t + long(bg) * D + lane * 8);
     }
 
-    // ---- the state, loaded alongside (positions fit in 32 bits) ----------------------
+    // ---- the state (positions fit in 32 bits) and the visible rows ----------------------
     const int p = int(c.pos[bg]);
     const int cnt = c.count[bg];
     const int X = INGEST ? c.nx_slot[bg] : -1;
@@ -294,324 +386,333 @@ void decode_step_kernel(
     const int t = INGEST ? p : p - 1;
     const int tslot = t >= 0 ? t % w : 0;
     const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
-    // ingest operands every wave fetches (the last to arrive commits them): the new
-    // token's row chunk, the score of the token leaving next, and the weakest of this
-    // split's segment entries in the post-step state (slot X holding the newcomer)
-    u32x4 nk = u32x4{}, nv = u32x4{};
+    const int ns = t >= 0 ? min(s, t + 1) : 0;                  // sink rows
+    const bool ring_full = t - s + 1 >= w;                      // every ring slot visible
+    // ring slot r holds token t - d, d = (tslot - r) mod w: visible when >= s
+    auto ring_ok = [&](int r) {
+        const int d = tslot - r + (tslot < r ? w : 0);
+        return (r < w) & (d <= t - s);
+    };
+    auto head_ok = [&](int slot) {
+        return (slot < ns) | (unsigned(slot - s) < unsigned(new_cnt));
+    };
+    // head chunks holding a visible row: [0, ha) U [hb, he)
+    const int ha = (ns + RW - 1) / RW;
+    const int hb = s / RW;
+    const int he = new_cnt > 0 ? (s + new_cnt + RW - 1) / RW : hb;
+    const bool merged = hb <= ha;
+    const int nvh = merged ? max(ha, he) : ha + (he - hb);
+    const int e_hi = min(e_lo + per, nr + nvh);
+    auto head_chunk = [&](int hi) { return (merged || hi < ha) ? hi : hb + hi - ha; };
+    // head chunk k: invalid rows re-read the chunk's first visible one; in the
+    // post-ingest state the segment slot the leaving token takes reads it from its
+    // ring slot (the new token's sink row is patched in LDS once it has landed)
+    const int xslot = (INGEST && X >= 0) ? s + X : -1;
+    auto chunk_rows = [&](int ent, uint32_t (&roff)[NL]) {
+        if (ent < nr) {
+            ring_rows(ent, roff);
+        } else {
+            const int k = head_chunk(ent - nr);
+            const int fv = (RW * k < ns) ? RW * k : max(RW * k, s);
+#pragma unroll
+            for (int x = 0; x < NL; ++x) {
+                int slot = RW * k + (64 * x + lane) / CPR;
+                slot = head_ok(slot) ? slot : fv;
+                slot = (slot == xslot) ? s + C + tslot : slot;
+                roff[x] = uint32_t(slot) * (D * 2);
+            }
+        }
+    };
+    if (!early0 && ent0 < e_hi) {
+        uint32_t roff[NL];
+        chunk_rows(ent0, roff);
+        load_lds(roff);
+    }
+    // ingest operands consumed at the end: the score of the token leaving at the next
+    // step and the leaving token's row (lanes < D/8 of wave 0)
     float r1 = 0.0f;
-    float wsc = INFINITY;
-    int wtk = -1, wsl = -1;
+    u32x4 lk = u32x4{}, lv = u32x4{};
     if (INGEST) {
-        if (lane < CPR) {
-            nk = *reinterpret_cast<const u32x4*>(k_t + long(bg) * D + lane * 8);
-            nv = *reinterpret_cast<const u32x4*>(v_t + long(bg) * D + lane * 8);
-        }
         if (t + 1 - w >= s) r1 = c.ring_score[long(bg) * w + (t + 1) % w];
-        const int e = slot0 + lane - s;
-        if (C > 0 && new_cnt == C && e >= 0 && e < C) {
-            wsc = (e == X) ? rl : c.ret_score[long(bg) * C + e];
-            wtk = (e == X) ? t - w : c.ret_idx[long(bg) * C + e];
-            wsl = e;
+        if (X >= 0 && wave == 0 && lane < CPR) {
+            const long rr = long(s + C + tslot) * D + lane * 8;
+            lk = *reinterpret_cast<const u32x4*>(c.k + base + rr);
+            lv = *reinterpret_cast<const u32x4*>(c.v + base + rr);
         }
     }
 
-    // rows that differ in the post-ingest state: the new token (ring slot t mod w and,
-    // while t < s, sink slot t) comes from the inputs; segment slot X holds the leaving
-    // token, still in ring slot t mod w.  At most three slots, each checked once.
-    int fs[3] = {-1, -1, -1};
-    if (INGEST) {
-        fs[0] = t < s ? t : -1;
-        fs[1] = X >= 0 ? s + X : -1;
-        fs[2] = s + C + tslot;
-#pragma unroll
-        for (int f = 0; f < 3; ++f) {
-            const int kk = fs[f] - slot0;                     // wave-uniform
-            if (fs[f] < 0 || kk < 0 || kk >= KPB || fs[f] >= S) continue;
-            const uint16_t* rk = (f == 1) ? c.k + base + long(s + C + tslot) * D : k_t + long(bg) * D;
-            if (l16 == (kk & 15)) {                           // q.k A operand rows
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    if (mt == (kk >> 4)) {
-#pragma unroll
-                        for (int kq = 0; kq < KS; ++kq)
-                            ka[mt][kq] = *reinterpret_cast<const bf16x8*>(rk + 32 * kq + 8 * q16);
-                    }
-                }
-            }
-        }
-    }
-    // validity of the 64 slots as a wave-wide bit mask (lane k tests slot slot0 + k)
-    uint64_t vmask;
-    {
-        const int cs = slot0 + lane;
-        bool ok = false;
-        if (cs < S && t >= 0) {
-            if (cs < s) {
-                ok = cs <= t;
-            } else if (cs < s + C) {
-                ok = (cs - s) < new_cnt;
-            } else {
-                // ring slot r holds token t - d, d = (tslot - r) mod w: valid when >= s
-                const int r = cs - s - C;
-                const int d = (r <= tslot) ? tslot - r : tslot - r + w;
-                ok = d <= t - s;
-            }
-        }
-        vmask = __ballot(ok);
-    }
-
-    // the wave owning the slot the leaving token takes also moves its row there
-    if (INGEST && X >= 0) {
-        const int lr = s + X - slot0;
-        if (lr >= 0 && lr < KPB && lane < D / 8) {
-            const long rr = base + long(s + C + tslot) * D + lane * 8;
-            const long dst = base + long(s + X) * D + lane * 8;
-            *reinterpret_cast<uint4*>(c.k + dst) = *reinterpret_cast<const uint4*>(c.k + rr);
-            *reinterpret_cast<uint4*>(c.v + dst) = *reinterpret_cast<const uint4*>(c.v + rr);
-        }
-    }
-
-    // ---- s^T = K q^T: rows = keys 16mt + 4q16 + r, column = head l16 -----------------
-    f32x4 sacc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        sacc[mt] = f32x4{};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) sacc[mt] = mfma16(ka[mt][kk], qf[kk], sacc[mt]);
-    }
+    // ---- this wave's chunks: online softmax.  The reference maximum of a head moves
+    //      only when exceeded by more than 2^8 in the exponent, so p <= 256 and o is
+    //      rarely rescaled; the final division by the sum cancels the choice exactly ----
     const float csc = kLog2e * rsqrtf(float(D));
-    float x[4][4];
-    float m = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const bool ok = (vmask >> (16 * mt + 4 * q16 + r)) & 1ull;
-            x[mt][r] = ok ? sacc[mt][r] * csc : -INFINITY;
-            m = fmaxf(m, x[mt][r]);
-        }
-    }
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    const float msafe = (m == -INFINITY) ? 0.0f : m;
-    // p = p_hi + p_lo, both bf16: the P.V product keeps ~16 mantissa bits of p.
-    // B operand of chunk cc, element e: key 32cc + 16(e/4) + 4q16 + e%4
-    float l = 0.0f;
-    bf16x8 pf[2], pl[2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(x[mt][r] - msafe);
-            l += pr;
-            const __bf16 hi = (__bf16)pr;
-            pf[mt >> 1][(mt & 1) * 4 + r] = hi;
-            pl[mt >> 1][(mt & 1) * 4 + r] = (__bf16)(pr - float(hi));
-        }
-    }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-
-    // ---- V tile landed; substituted rows overwrite theirs --------------------------------
-    __builtin_amdgcn_s_waitcnt(0);
-    if (INGEST) {
-#pragma unroll
-        for (int f = 0; f < 3; ++f) {
-            const int kk = fs[f] - slot0;
-            if (fs[f] < 0 || kk < 0 || kk >= KPB || fs[f] >= S) continue;
-            const uint16_t* rv = (f == 1) ? c.v + base + long(s + C + tslot) * D : v_t + long(bg) * D;
-            if (lane < CPR)
-                Vw[kk * CPR + lane] = *reinterpret_cast<const u32x4*>(rv + 8 * (lane ^ vswz<D>(kk)));
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- o^T = V^T p^T: rows = dims 16dt + 4q16 + r, column = head l16.  A operand
-    //      element e of lane (q16, i): V[32cc + 16(e/4) + 4q16 + e%4][16dt + i], two
-    //      transposing reads of 4 keys; lane j of the 16 reads key .. + j/4, dims
-    //      16dt + 4(j%4) .. +3 --------------------------------------------------------------
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    float m_ref = -INFINITY;       // reference max of head l16 (raw logits)
+    float l_run = 0.0f;            // this lane's share of the running sum
     f32x4 oacc[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        oacc[dt] = f32x4{};
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{};
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    for (int ent = ent0; ent < e_hi; ent += NW) {
+        __builtin_amdgcn_s_waitcnt(0);        // this chunk's direct loads have landed
+        const bool is_ring = ent < nr;
+        const int k0 = is_ring ? RW * ent : RW * head_chunk(ent - nr);   // first row / slot
+        // visible rows of the chunk as a bit mask (lane j < 32 tests row k0 + j)
+        const bool okj = is_ring ? ring_ok(k0 + (lane & 31)) : head_ok(k0 + (lane & 31));
+        const uint32_t vmask = uint32_t(__ballot(okj));
+        // rows holding the new token: ring slot t mod w, or sink slot t while t < s
+        int pr = -1;
+        if (is_ring) {
+            // until the ring is full some of its slots were never written: zero their V
+            // rows so that p = 0 meets finite values
+            if (!ring_full) {
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+                for (int x = 0; x < NL; ++x) {
+                    const int pidx = 64 * x + lane;
+                    if (!((vmask >> (pidx / CPR)) & 1u)) Vt[pidx] = u32x4{};
+                }
+            }
+            if (INGEST && t >= s) pr = tslot - k0;
+        } else if (INGEST && t < s) {
+            pr = t - k0;
+        }
+        if (INGEST && pr >= 0 && pr < RW && lane < CPR) {
+            Kt[pr * CPR + (lane ^ kswz<D>(pr))] = nk;
+            Vt[pr * CPR + (lane ^ vswz<D>(pr))] = nvv;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // s^T = K q^T: rows = keys 16mt + 4q16 + r of the chunk, column = head l16
+        f32x4 sacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = f32x4{};
+            const int row = 16 * mt + l16;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, Kt[row * CPR + ((4 * kk + q16) ^ kswz<D>(row))]);
+                sacc[mt] = mfma16(a, qf[kk], sacc[mt]);
+            }
+        }
+        if (vmask != 0xffffffffu) {
+            const uint32_t lm = vmask >> (4 * q16);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (!((lm >> (16 * mt + r)) & 1u)) sacc[mt][r] = -INFINITY;
+        }
+        float mc = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+        mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
+        mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+        // NaN (both -inf: nothing visible yet) compares false: no move
+        const bool move = (mc - m_ref) * csc > 8.0f;
+        if (__ballot(move) != 0ull) {
+            const float m_new = move ? mc : m_ref;
+            const float alpha = move ? __builtin_amdgcn_exp2f((m_ref - m_new) * csc) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            m_ref = m_new;
+        }
+        const float moff = (m_ref == -INFINITY) ? 0.0f : -m_ref * csc;
+        // B operand element e: key 16(e/4) + 4q16 + e%4
+        bf16x8 pf;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], csc, moff));
+                l_run += pe;
+                pf[mt * 4 + r] = (__bf16)pe;
+            }
+        }
+        // o^T += V^T p^T: rows = dims 16dt + 4q16 + r, column = head l16.  A operand
+        // element e of lane (q16, i): V[16(e/4) + 4q16 + e%4][16dt + i], two transposing
+        // reads of 4 keys; lane j of 16 reads key .. + j/4, dims 16dt + 4(j%4) .. +3
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
             bf16x8 a;
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2) {
-                const int key = 32 * cc + 16 * r2 + 4 * q16 + (l16 >> 2);
+                const int key = 16 * r2 + 4 * q16 + (l16 >> 2);
                 const int d0 = 16 * dt + 4 * (l16 & 3);
                 const __bf16* src = reinterpret_cast<const __bf16*>(
-                                        &Vw[key * CPR + ((d0 >> 3) ^ vswz<D>(key))]) + (d0 & 7);
+                                        &Vt[key * CPR + ((d0 >> 3) ^ vswz<D>(key))]) + (d0 & 7);
                 const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) v4i16*)(src));
                 const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[4 * r2 + e] = b4[e];
             }
-            oacc[dt] = mfma16(a, pf[cc], oacc[dt]);
-            oacc[dt] = mfma16(a, pl[cc], oacc[dt]);
+            oacc[dt] = mfma16(a, pf, oacc[dt]);
+        }
+        // the next chunk's rows into the tiles once their reads are done
+        if (ent + NW < e_hi) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            uint32_t roff[NL];
+            chunk_rows(ent + NW, roff);
+            load_lds(roff);
         }
     }
-    // ---- the waves' partials combine into one per workgroup: o [G][D] at 0, (max, sum)
-    //      of head h at G*D + 2h, the weakest segment entry at G*D + 2G -----------------
-    constexpr int kPart = decode_part_floats(G, D);             // floats per split
-    __amdgpu_buffer_rsrc_t prs = part_rsrc(part + long(bg) * nsplit * kPart);
-    if (INGEST) wave_weakest(wsc, wtk, wsl);
-    float* xw = reinterpret_cast<float*>(Vs[1]);               // wave 1's, read by now
-    if (wave == 1) {
-        if (l16 < G) {
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    // the weakest entry of the post-step segment when it holds C entries (slot X
+    // holding the newcomer), this wave's share
+    if (INGEST) {
+        float wsc = INFINITY;
+        int wtk = -1, wsl = -1;
+        if (C > 0 && new_cnt == C) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<f32x4*>(&xw[l16 * D + 16 * dt + 4 * q16]) = oacc[dt];
-            if (q16 == 0) *reinterpret_cast<f32x2*>(&xw[G * D + 2 * l16]) = f32x2{m, l};
+            for (int i = 0; i < kScan; ++i) {
+                const int e = tid + i * 64 * NW;
+                const float sc = (e == X) ? rl : sc_e[i];
+                const int tk = (e == X) ? t - w : tk_e[i];
+                if (e < C && weaker(sc, tk, wsc, wtk)) { wsc = sc; wtk = tk; wsl = e; }
+            }
+            wave_weakest(wsc, wtk, wsl);
         }
-        if (INGEST && lane == 0)
-            *reinterpret_cast<u32x4*>(&xw[G * D + 2 * G]) =
-                u32x4{__float_as_uint(wsc), uint32_t(wtk), uint32_t(wsl), 0u};
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const int pbase = sp * kPart * 4;                          // bytes
-        if (l16 < G) {
-            const f32x2 ml1 = *reinterpret_cast<const f32x2*>(&xw[G * D + 2 * l16]);
-            const float Mn = fmaxf(m, ml1[0]);
-            const float Ms = (Mn == -INFINITY) ? 0.0f : Mn;
-            const float a0 = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - Ms);
-            const float a1 = (ml1[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml1[0] - Ms);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xw[l16 * D + 16 * dt + 4 * q16]);
-                const f32x4 o4 = oacc[dt] * a0 + o1 * a1;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), prs,
-                                                       pbase + (l16 * D + 16 * dt + 4 * q16) * 4,
-                                                       0, kSc1);
-            }
-            if (q16 == 0) {
-                const f32x2 ml = {Mn, l * a0 + ml1[1] * a1};
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), prs,
-                                                      pbase + (G * D + 2 * l16) * 4, 0, kSc1);
-            }
-        }
-        if (INGEST && lane == 0) {
-            const u32x4 w1 = *reinterpret_cast<const u32x4*>(&xw[G * D + 2 * G]);
-            if (weaker(__uint_as_float(w1[0]), int(w1[1]), wsc, wtk)) {
-                wsc = __uint_as_float(w1[0]);
-                wtk = int(w1[1]);
-                wsl = int(w1[2]);
-            }
-            const u32x4 wt = {__float_as_uint(wsc), uint32_t(wtk), uint32_t(wsl), 0u};
-            __builtin_amdgcn_raw_buffer_store_b128(wt, prs, pbase + (G * D + 2 * G) * 4, 0, kSc1);
+        if (lane == 0) {
+            wk_sc[wave] = wsc;
+            wk_tk[wave] = wtk;
+            wk_sl[wave] = wsl;
         }
     }
 
-    // ---- this step's share of the deferred batch ---------------------------------------
+    // ---- this step's share of the deferred batch (wave-private LDS) ----------------------
     if (INGEST && t == u + w - 3) {
-        __syncthreads();                          // wave 1's partial read: its rows are free
-        float* Y = reinterpret_cast<float*>(Vw);
-        const int nch = (t - 1 - u + kWaveScoreTile - 1) / kWaveScoreTile;
-        for (int ch = sp * NWV + wave; ch < nch; ch += nsplit * NWV)
-            score_deferred_chunk<D>(c, bg, g, s, w, C, S, t, u, ch, k_t, v_t, cnn, Y);
+        __builtin_amdgcn_s_waitcnt(0);
+        const int nchs = (t - 1 - u + kWaveScoreTile - 1) / kWaveScoreTile;
+        for (int ch = sp * NW + wave; ch < nchs; ch += nsplit * NW)
+            score_deferred_chunk<D>(c, bg, g, s, w, C, S, t, u, ch, k_t, v_t, cnn,
+                                    reinterpret_cast<float*>(Kt), reinterpret_cast<float*>(Vt));
     }
 
-    // ---- arrival: the last workgroup of (b, g) merges and finishes the step ---------------
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);            // partials, row copies, scores complete
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    int* last_arrival = reinterpret_cast<int*>(Vs[1]);        // every LDS use is over
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(c.arrive + bg, 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        *last_arrival = (old == nsplit - 1) ? 1 : 0;
+    // ---- the waves' partials combine in LDS: wave wv's o [G][D] in its K region,
+    //      (max, sum) of head h (log2 units) at 2h of its V region ----------------------------
+    __syncthreads();                              // every tile and scorer row is free
+    if (l16 < G) {
+        float* po = reinterpret_cast<float*>(Kt);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<f32x4*>(&po[l16 * D + 16 * dt + 4 * q16]) = oacc[dt];
+        if (q16 == 0)
+            *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(Vt) + 2 * l16) =
+                f32x2{m_ref == -INFINITY ? -INFINITY : m_ref * csc, l_run};
     }
     __syncthreads();
-    if (*last_arrival == 0) return;
-
-    // the splits' weakest segment entries, loaded alongside the first merge round
-    u32x4 wt0 = u32x4{__float_as_uint(INFINITY), ~0u, ~0u, 0u};
-    if (INGEST && wave == 0 && lane < nsplit)
-        wt0 = __builtin_amdgcn_raw_buffer_load_b128(prs, lane * kPart * 4 + (G * D + 2 * G) * 4,
-                                                    0, kSc1);
-    // merge: thread handles head hh = tid / TPH, dims [d0, d0 + DPL), online over the
-    // splits in split order; coherent loads CH splits at a time
-    {
-        constexpr int NT = 64 * NWV;
-        constexpr int TPH = (G * D >= NT ? NT : G * D) / G;      // threads per head
-        constexpr int DPL = D / TPH;              // dims per thread: 1, 2 or a multiple of 4
-        constexpr int NQ = DPL >= 4 ? DPL / 4 : 1;        // loads of o per split
-        constexpr int CH = 96 / (DPL + 2) > 0 ? 96 / (DPL + 2) : 1;   // splits per round
-        const bool active = tid < TPH * G;
-        const int hh = active ? tid / TPH : 0;
-        const int d0 = active ? (tid % TPH) * DPL : 0;
-        float M = -INFINITY, L = 0.0f;
-        float o[DPL];
+    // thread -> head hh, dims [d0, d0 + DPL); waves merged in order (deterministic)
+    constexpr int NT = 64 * NW;
+    constexpr int TPH = (G * D >= NT ? NT : G * D) / G;          // threads per head
+    constexpr int DPL = D / TPH;                                 // 1, 2 or 4
+    const bool active = tid < TPH * G;
+    const int hh = active ? tid / TPH : 0;
+    const int d0 = active ? (tid % TPH) * DPL : 0;
+    float M = -INFINITY, L = 0.0f;
+    float o[DPL];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
-        for (int c0 = 0; c0 < nsplit; c0 += CH) {
-            f32x2 ml[CH];
-            f32x4 ov[CH][NQ];
+    for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+    auto merge_in = [&](float ms, float ls, const float* ov) {
+        const float Mn = fmaxf(M, ms);
+        const float Ms = (Mn == -INFINITY) ? 0.0f : Mn;
+        const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Ms);
+        const float f = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - Ms);
+        L = L * a + f * ls;
 #pragma unroll
-            for (int q = 0; q < CH; ++q) {
-                const int pb = min(c0 + q, nsplit - 1) * kPart * 4;
-                ml[q] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                      prs, pb + (G * D + 2 * hh) * 4, 0, kSc1));
+        for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + f * ov[e];
+        M = Mn;
+    };
 #pragma unroll
-                for (int e = 0; e < NQ; ++e) {
-                    const int off = pb + (hh * D + d0 + 4 * e) * 4;
-                    if (DPL >= 4) {
-                        ov[q][e] = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kSc1));
-                    } else if (DPL == 2) {
-                        const f32x2 t2 = __builtin_bit_cast(
-                            f32x2, __builtin_amdgcn_raw_buffer_load_b64(prs, off, 0, kSc1));
-                        ov[q][e] = f32x4{t2[0], t2[1], 0.0f, 0.0f};
-                    } else {
-                        const float t1 = __builtin_bit_cast(
-                            float, __builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, kSc1));
-                        ov[q][e] = f32x4{t1, 0.0f, 0.0f, 0.0f};
-                    }
-                }
-            }
+    for (int wv = 0; wv < NW; ++wv) {
+        const float* po = reinterpret_cast<const float*>(Ks[wv]);
+        const float* pm = reinterpret_cast<const float*>(Vs[wv]);
+        float ov[DPL];
 #pragma unroll
-            for (int q = 0; q < CH; ++q) {
-                // splits past the last one re-read it and weigh in as nothing
-                const float ms = (c0 + q < nsplit) ? ml[q][0] : -INFINITY;
-                const float ls = ml[q][1];
-                const float Mn = fmaxf(M, ms);
-                const float Ms = (Mn == -INFINITY) ? 0.0f : Mn;
-                const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Ms);
-                const float f = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - Ms);
-                L = L * a + f * ls;
+        for (int e = 0; e < DPL; ++e) ov[e] = po[hh * D + d0 + e];
+        merge_in(pm[2 * hh], pm[2 * hh + 1], ov);
+    }
+    // the weakest entry of the post-step segment, over the waves in order
+    float wsc = INFINITY;
+    int wtk = -1, wsl = -1;
+    if (INGEST) {
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + f * ov[q][e / 4][e % 4];
-                M = Mn;
+        for (int wv = 0; wv < NW; ++wv) {
+            if (weaker(wk_sc[wv], wk_tk[wv], wsc, wtk)) {
+                wsc = wk_sc[wv];
+                wtk = wk_tk[wv];
+                wsl = wk_sl[wv];
             }
         }
-        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-        __bf16* orow = reinterpret_cast<__bf16*>(out_t) + (long(b) * Hq + g * G + hh) * D + d0;
+    }
+
+    if (nsplit > 1) {
+        // ---- split partial out, coherent; the last workgroup of (b, g) merges the
+        //      splits in split order and finishes the step --------------------------------
+        __amdgpu_buffer_rsrc_t prs = part_rsrc(part + long(bg) * nsplit * PW);
         if (active) {
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(o[e] * inv);
+            for (int e = 0; e < DPL; ++e)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[e]), prs,
+                                                      (sp * PW + hh * D + d0 + e) * 4, 0, kSc1);
+            if (d0 == 0)
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{M, L}), prs,
+                                                      (sp * PW + G * D + 2 * hh) * 4, 0, kSc1);
         }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);        // partials and scores complete
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(c.arrive + bg, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = (old == nsplit - 1) ? 1 : 0;
+        }
+        __syncthreads();
+        if (last_flag == 0) return;
+        M = -INFINITY;
+        L = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+        constexpr int CH = 8;                     // splits loaded per round
+        for (int c0 = 0; c0 < nsplit; c0 += CH) {
+            f32x2 ml[CH];
+            float ov[CH][DPL];
+#pragma unroll
+            for (int qq = 0; qq < CH; ++qq) {
+                const int pb = min(c0 + qq, nsplit - 1) * PW;
+                ml[qq] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       prs, (pb + G * D + 2 * hh) * 4, 0, kSc1));
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    ov[qq][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        prs, (pb + hh * D + d0 + e) * 4, 0, kSc1));
+            }
+#pragma unroll
+            for (int qq = 0; qq < CH; ++qq)   // splits past the last weigh in as nothing
+                merge_in((c0 + qq < nsplit) ? ml[qq][0] : -INFINITY, ml[qq][1], ov[qq]);
+        }
+    }
+
+    // ---- o_t, then the rest of the ingest ----------------------------------------------
+    if (active) {
+        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+        __bf16* orow = reinterpret_cast<__bf16*>(out_t) + (long(b) * Hq + g * G + hh) * D + d0;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(o[e] * inv);
     }
     if (INGEST && wave == 0) {
-        // weakest of the post-step segment: over the splits' weakest entries
-        float bs = __uint_as_float(wt0[0]);
-        int bt = int(wt0[1]), bl = int(wt0[2]);
-        for (int q = lane + 64; q < nsplit; q += 64) {
-            const u32x4 wt = __builtin_amdgcn_raw_buffer_load_b128(
-                prs, q * kPart * 4 + (G * D + 2 * G) * 4, 0, kSc1);
-            const float sc = __uint_as_float(wt[0]);
-            if (weaker(sc, int(wt[1]), bs, bt)) { bs = sc; bt = int(wt[1]); bl = int(wt[2]); }
+        // the leaving token's row into its segment slot; no workgroup reads that slot's
+        // old contents in this step, and every read of the ring slot is complete
+        if (X >= 0 && lane < CPR) {
+            const long dst = base + long(s + X) * D + lane * 8;
+            *reinterpret_cast<u32x4*>(c.k + dst) = lk;
+            *reinterpret_cast<u32x4*>(c.v + dst) = lv;
         }
-        wave_weakest(bs, bt, bl);
-        ingest_commit<D>(c, bg, s, w, C, S, t, cnt, X, rl, u, bl, bs, r1, nk, nv);
+        ingest_commit<D>(c, bg, s, w, C, S, t, cnt, X, rl, u, wsl, wsc, r1, nk, nvv);
     }
-    if (tid == 0) __hip_atomic_store(c.arrive + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (nsplit > 1 && tid == 0)
+        __hip_atomic_store(c.arrive + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -638,7 +739,7 @@ hipError_t launch_decode(const Shape& sh, bool ingest, const uint16_t* q_t, cons
     if (cnn != nullptr) cn = *cnn;
 #define LTE_DECODE_G(DD, GG, ING)                                                               \
     case GG:                                                                                    \
-        hipLaunchKernelGGL((decode_step_kernel<DD, GG, ING>), grid, dim3(64 * NWV), 0, st,       \
+        hipLaunchKernelGGL((decode_step_kernel<DD, GG, ING>), grid, dim3(64 * kDecodeWaves), 0, st,       \
                            sh.Hq, sh.Hkv, sh.s, sh.w, sh.C, sh.S, nsplit, q_t, k_t, v_t, cn,     \
                            cache, part, out_t);                                                 \
         break;

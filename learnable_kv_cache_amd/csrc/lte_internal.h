@@ -126,13 +126,22 @@ inline size_t select_scratch_words(int64_t T) {
     return size_t(4 * Tp) + align256(size_t(2 * select_nsnap_max(T) * select_words(T)) * 4) / 4;
 }
 
-// Decode split-K: cache slots per workgroup (two waves of 64) and the number of splits.
-constexpr int kDecodeSplitKeys = 128;
-inline int decode_nsplit(const Shape& sh) { return (sh.S + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
-// Floats per split partial: o [G][D], then (max, sum) per head and the split's
-// weakest segment entry (score, token, slot), padded to 16 bytes.
+// Decode split-K.  A workgroup (8 waves) attends over a contiguous range of one
+// (b, g)'s visible rows; with at least 128 (b, g) pairs there is one workgroup
+// per pair and the waves merge in LDS, otherwise each pair is split over up to
+// 256 / (B * Hkv) workgroups of at least 128 slots, merged by the last to finish.
+constexpr int kDecodeWaves = 8;
+inline int decode_nsplit(const Shape& sh) {
+    const long bg = long(sh.B) * sh.Hkv;
+    if (bg >= 128) return 1;
+    const long by_grid = (256 + bg - 1) / bg;
+    const long by_rows = (sh.S + 127) / 128;
+    const long n = by_grid < by_rows ? by_grid : by_rows;
+    return int(n < 1 ? 1 : n);
+}
+// Floats per split partial: o [G][D], then (max, sum) per head, padded to 16 bytes.
 __host__ __device__ constexpr int decode_part_floats(int G, int D) {
-    return G * D + ((2 * G + 3 + 3) & ~3);
+    return G * D + ((2 * G + 3) & ~3);
 }
 
 struct WsLayout {

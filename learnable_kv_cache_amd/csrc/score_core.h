@@ -139,13 +139,15 @@ __device__ __forceinline__ void score_chunk(unsigned char* buf, const float* w2s
 // arithmetic per token as score_chunk: layer 1 on v_mfma_f32_32x32x16_bf16
 // over the 32 rows t0-2 .. t0+29, with W1's bf16 operands built from the fp32
 // weights; a token's score does not depend on how tokens are grouped.
-//   Y        LDS of kWaveScoreBytes, wave-private
+//   Ya       LDS of kWaveScoreBytesA: layer-1 taps 0 and 1 [32 rows][64], wave-private
+//   Yb       LDS of kWaveScoreBytesB: layer-1 tap 2 [32 rows][32], wave-private
 //   w1g      fp32 W1 of this head [hidden][2D][3]; w2g [hidden][3]
 constexpr int kWaveScoreTile = 28;
-constexpr int kWaveScoreBytes = 32 * 96 * 4;
+constexpr int kWaveScoreBytesA = 32 * 64 * 4;
+constexpr int kWaveScoreBytesB = 32 * 32 * 4;
 
 template <int D, class XRow, class AZero, class Store>
-__device__ __forceinline__ void score_wave(float* Y, const float* __restrict__ w1g,
+__device__ __forceinline__ void score_wave(float* Ya, float* Yb, const float* __restrict__ w1g,
                                            const float* __restrict__ b1g,
                                            const float* __restrict__ w2g, float b2g, int t0,
                                            int tlo, int thi, XRow x_row, AZero a_zero,
@@ -175,7 +177,8 @@ __device__ __forceinline__ void score_wave(float* Y, const float* __restrict__ w
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int row = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-            Y[row * 96 + tp * 32 + (lane & 31)] = acc[e];
+            if (tp < 2) Ya[row * 64 + tp * 32 + (lane & 31)] = acc[e];
+            else Yb[row * 32 + (lane & 31)] = acc[e];
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -189,11 +192,11 @@ __device__ __forceinline__ void score_wave(float* Y, const float* __restrict__ w
         const int t = t0 - 2 + r;
         float a = 0.0f;
         if (!a_zero(t)) {
-            const float h = b1g[o] + Y[(r - 1) * 96 + o] + Y[r * 96 + 32 + o] +
-                            Y[(r + 1) * 96 + 64 + o];
+            const float h = b1g[o] + Ya[(r - 1) * 64 + o] + Ya[r * 64 + 32 + o] +
+                            Yb[(r + 1) * 32 + o];
             a = gelu_erf(h);
         }
-        Y[r * 96 + 32 + o] = a;
+        Ya[r * 64 + 32 + o] = a;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -203,12 +206,12 @@ __device__ __forceinline__ void score_wave(float* Y, const float* __restrict__ w
         const int t = t0 + lane;
         if (t >= tlo && t <= thi) {
             float z = b2g;
-            const float* a = Y + 32;
+            const float* a = Ya + 32;
             const int r = lane + 2;
 #pragma unroll 8
             for (int o = 0; o < kHidden; ++o) {
-                z += w2g[o * 3 + 0] * a[(r - 1) * 96 + o] + w2g[o * 3 + 1] * a[r * 96 + o] +
-                     w2g[o * 3 + 2] * a[(r + 1) * 96 + o];
+                z += w2g[o * 3 + 0] * a[(r - 1) * 64 + o] + w2g[o * 3 + 1] * a[r * 64 + o] +
+                     w2g[o * 3 + 2] * a[(r + 1) * 64 + o];
             }
             store(t, 1.0f / (1.0f + expf(-z)));
         }

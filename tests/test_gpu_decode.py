@@ -118,6 +118,15 @@ def test_decode_d128_gqa8():
     run_decode_parity(B, T, n, Hq, Hkv, D, s, w, C, q, k, v, cnn)
 
 
+def test_decode_split_workgroups():
+    """Few (batch, KV head) pairs and a 304-slot cache: each pair's rows are split over three
+    workgroups merged by the last to finish; the segment overflows and a deferred batch
+    fires at t = 495."""
+    B, T, n, Hq, Hkv, D, s, w, C = 1, 300, 220, 8, 2, 128, 4, 200, 100
+    q, k, v, cnn = synth.random_case(17, B, T + n, Hq, Hkv, D, b2=0.05)
+    run_decode_parity(B, T, n, Hq, Hkv, D, s, w, C, q, k, v, cnn, every=3)
+
+
 def test_decode_full_size():
     """Decode at B32, 4096-token prompt, Hq16 Hkv4 D128 s4 w512 C512, 512 steps (one deferred
     scoring batch fires at t = 4603); batches 0 and 21 checked against the oracle."""
