@@ -12,8 +12,13 @@ Reported: prefill tokens/s (``value``) and decode microseconds per layer-step,
 each with the roofline of its dominant kernel, next to the CPU oracle timed on
 this host.
 
+Beside it, the same engine as the two comparators of the LTE paper's Figure 4
+(sink + sliding-window attention with no retained segment, and full causal
+attention as a window covering the whole sequence), timed on the same inputs.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
-                       [--no-cpu-baseline] [--no-decode] [--copy-calibration MIB]
+                       [--no-cpu-baseline] [--no-decode] [--no-comparators]
+                       [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -46,6 +51,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="sequences the oracle runs for the CPU baseline (0: one per core)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -180,6 +186,87 @@ def _cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+# ---------------------------------------------------------------------------
+# Figure 4 comparators: the same engine with no retained segment
+# ---------------------------------------------------------------------------
+
+def _graph_us_per_step(layer, caches, qs, ks, vs, cnn, ws, reps=3):
+    """Decode microseconds per layer-step of a HIP-graph replay over caches."""
+    import torch
+    out = torch.empty_like(qs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in caches:
+            layer.decode_step(qs[0], ks[0], vs[0], cnn, c, ws, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(len(qs)):
+            for c in caches:
+                layer.decode_step(qs[t], ks[t], vs[t], cnn, c, ws, out)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e3 / (len(qs) * len(caches)))
+    return best
+
+
+def comparators(inp, wl, T, dev, ndec=64):
+    """Sink + SWA (capacity 0) and full causal attention (window = T + ndec, capacity 0)
+    run through the same kernels on the same q, k, v: prefill attention time and
+    decode time per layer-step (caches rotated past the last-level cache)."""
+    import torch
+    from learnable_kv_cache_amd import lte
+    B, s = wl.B, wl.sink
+    G = wl.Hq // wl.Hkv
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    qp, kp, vp = (x[:, :T].contiguous() for x in (q, k, v))
+    dq = [q[:, T + t].contiguous() for t in range(ndec)]
+    dk = [k[:, T + t].contiguous() for t in range(ndec)]
+    dv = [v[:, T + t].contiguous() for t in range(ndec)]
+    cnn = lte.CNN(inp["cnn"], dev)
+    zero_scores = torch.zeros((B, wl.Hkv, T), dtype=torch.float32, device=dev)
+    res = {}
+    for name, w in (("swa", wl.window), ("full", T + ndec)):
+        layer = lte.Layer(lte.Config(B, wl.Hq, wl.Hkv, wl.D, s, w, 0))
+        ws = layer.alloc_workspace(T, dev)
+        out = torch.empty_like(qp)
+        cache = layer.alloc_cache(dev)
+        layer.prefill(qp, kp, vp, score_override=zero_scores, cache=cache, workspace=ws, out=out)
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            layer.prefill_attend(qp, kp, vp, ws, out)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        att_ms = float(np.median(times))
+        i = np.arange(T, dtype=np.float64)
+        # window keys plus the sink tokens that lie below the window
+        keys = np.minimum(i + 1, w) + np.minimum(np.minimum(s, i + 1), np.maximum(0, i - w + 1))
+        flops = 4.0 * wl.D * G * B * wl.Hkv * float(keys.sum())
+        L = math.ceil(2 * MALL_BYTES / layer.cache_bytes()) + 1
+        caches = [cache] + [cache.clone() for _ in range(L - 1)]
+        us = _graph_us_per_step(layer, caches, dq, dk, dv, cnn, ws)
+        nvis = min(T + ndec // 2, w) + (s if w < T else 0)
+        step_bytes = B * wl.Hkv * nvis * wl.D * 2 * 2 + 4 * B * wl.Hq * wl.D
+        res[name] = {"window": w, "capacity": 0, "prefill_attend_ms": att_ms,
+                     "prefill_attend_tflops": flops / (att_ms * 1e-3) / 1e12,
+                     "decode_us_per_step": us, "decode_layers_rotated": L,
+                     "decode_GBps": step_bytes / (us * 1e-6) / 1e9}
+        del caches, cache, ws, out
+        torch.cuda.empty_cache()
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -367,6 +454,12 @@ def main():
                              "decode_step", os.path.join(ROOT, "learnable_kv_cache_amd", "csrc",
                                                          "decode.hip"))},
         }
+    if not args.no_comparators and not args.no_decode:
+        cmp = comparators(inp, wl, T, dev, ndec=min(64, ndec))
+        cmp["lte"] = {"window": wl.window, "capacity": wl.capacity, "prefill_attend_ms": att_ms,
+                      "prefill_attend_tflops": achieved / 1e12,
+                      "decode_us_per_step": result["decode"]["us_per_step"]}
+        result["comparators"] = cmp
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, T, args.cpu_sample)
     print(json.dumps(result), flush=True)
