@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     constexpr int DT = D / 16;                 // p.v output tiles
     constexpr int CPR = TL::CPR;
     constexpr int PW = decode_part_floats(G, D);
-    constexpr int kScan = kMaxCapacity / (64 * NW);     // segment entries per thread
+    constexpr int kScan = (kMaxCapacity + 64 * NW - 1) / (64 * NW);   // segment entries per thread
     static_assert(G * D * 4 <= TL::kKW * 16 && 2 * G * 4 <= TL::kVW * 16, "wave partials fit");
     __shared__ __align__(16) u32x4 Ks[NW][TL::kKW];
     __shared__ __align__(16) u32x4 Vs[NW][TL::kVW];
@@ -441,6 +441,28 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         }
     }
 
+    // the weakest entry of the post-step segment when it holds C entries (slot X
+    // holding the newcomer), this wave's share
+    if (INGEST) {
+        float wsc = INFINITY;
+        int wtk = -1, wsl = -1;
+        if (C > 0 && new_cnt == C) {
+#pragma unroll
+            for (int i = 0; i < kScan; ++i) {
+                const int e = tid + i * 64 * NW;
+                const float sc = (e == X) ? rl : sc_e[i];
+                const int tk = (e == X) ? t - w : tk_e[i];
+                if (e < C && weaker(sc, tk, wsc, wtk)) { wsc = sc; wtk = tk; wsl = e; }
+            }
+            wave_weakest(wsc, wtk, wsl);
+        }
+        if (lane == 0) {
+            wk_sc[wave] = wsc;
+            wk_tk[wave] = wtk;
+            wk_sl[wave] = wsl;
+        }
+    }
+
     // ---- this wave's chunks: online softmax.  The reference maximum of a head moves
     //      only when exceeded by more than 2^8 in the exponent, so p <= 256 and o is
     //      rarely rescaled; the final division by the sum cancels the choice exactly ----
@@ -558,28 +580,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     }
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    // the weakest entry of the post-step segment when it holds C entries (slot X
-    // holding the newcomer), this wave's share
-    if (INGEST) {
-        float wsc = INFINITY;
-        int wtk = -1, wsl = -1;
-        if (C > 0 && new_cnt == C) {
-#pragma unroll
-            for (int i = 0; i < kScan; ++i) {
-                const int e = tid + i * 64 * NW;
-                const float sc = (e == X) ? rl : sc_e[i];
-                const int tk = (e == X) ? t - w : tk_e[i];
-                if (e < C && weaker(sc, tk, wsc, wtk)) { wsc = sc; wtk = tk; wsl = e; }
-            }
-            wave_weakest(wsc, wtk, wsl);
-        }
-        if (lane == 0) {
-            wk_sc[wave] = wsc;
-            wk_tk[wave] = wtk;
-            wk_sl[wave] = wsl;
-        }
-    }
-
     // ---- this step's share of the deferred batch (wave-private LDS) ----------------------
     if (INGEST && t == u + w - 3) {
         __builtin_amdgcn_s_waitcnt(0);
@@ -604,8 +604,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     __syncthreads();
     // thread -> head hh, dims [d0, d0 + DPL); waves merged in order (deterministic)
     constexpr int NT = 64 * NW;
-    constexpr int TPH = (G * D >= NT ? NT : G * D) / G;          // threads per head
+    constexpr int TPH0 = NT / G >= D ? D : NT / G;
+    constexpr int TPH = TPH0 >= 64 ? (TPH0 >= 128 ? 128 : 64) : (TPH0 >= 32 ? 32 : 16);  // threads per head
     constexpr int DPL = D / TPH;                                 // 1, 2 or 4
+    static_assert(TPH * G <= NT && DPL * TPH == D, "merge split");
     const bool active = tid < TPH * G;
     const int hh = active ? tid / TPH : 0;
     const int d0 = active ? (tid % TPH) * DPL : 0;
