@@ -37,7 +37,8 @@
  *   - Arguments are validated on the host before any launch; a failing call
  *     returns a status and leaves memory untouched.  A failed launch returns
  *     LTE_ERR_HIP.  No C++ exception crosses this interface.
- *   - Sequences of a batch have equal length.
+ *   - Sequences of a batch have equal length, except in lte_prefill_varlen,
+ *     after which each sequence decodes from its own position.
  *   - Supported: head_dim in {64, 128}; q_heads / kv_heads in {1, 2, 4, 8,
  *     16}; kv_heads <= 128; hidden == 32; 5 <= window <= 32768;
  *     0 <= sink <= 256; 0 <= capacity <= 4096; 1 <= T <= 32768 tokens per
@@ -94,7 +95,8 @@ typedef struct {
  *   ring_score  fp32  [B][Hkv][w]  score of the token in each ring slot,
  *                                  NaN while not yet scored
  *   count       int32 [B][Hkv]     valid retained slots
- *   pos         int64 [B][Hkv]     tokens ingested so far (all equal)
+ *   pos         int64 [B][Hkv]     tokens ingested so far (equal over the
+ *                                  heads of a sequence)
  *   next_unscored int64 [B][Hkv]   oldest token still lacking a score
  *   flags       int32 [B][Hkv]     bit 0: a token left the window unscored
  *   weak        int32 [B][Hkv]     slot of the weakest retained entry (lowest
@@ -173,6 +175,27 @@ int lte_prefill(const lte_config* cfg, int64_t T,
                 const lte_cnn* cnn, const float* score_override,
                 void* cache, void* workspace, size_t workspace_bytes,
                 uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prefill of a batch whose prompts differ in length.  Nothing in the method
+ * couples the sequences of a batch (scores, selection and cache are per
+ * sequence and head), so each is the prompt of its own length.  Arguments and
+ * layouts are those of lte_prefill
+ * with T the padded length, plus
+ *   seq_lens  device int32 [B]: sequence b's prompt is rows [0, T_b) of its
+ *       [T] rows, T_b = seq_lens[b] clamped to [1, T]
+ * Rows >= T_b of q, k, v (and of score_override) are never read; rows >= T_b
+ * of out are not written.  Sequence b's result is the one lte_prefill gives
+ * for its first T_b rows alone: its cache holds pos = T_b and
+ * next_unscored = max(T_b - 2, s), so later decode calls step every sequence
+ * from its own position.  The workspace views then hold sequence b's
+ * intermediates at indices < T_b only.
+ * ------------------------------------------------------------------------- */
+int lte_prefill_varlen(const lte_config* cfg, int64_t T, const int32_t* seq_lens,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const lte_cnn* cnn, const float* score_override,
+                       void* cache, void* workspace, size_t workspace_bytes,
+                       uint16_t* out, void* stream);
 
 /* The four stages lte_prefill runs, in order, exposed for timing and tests.
  * Each reads and writes the workspace views described above. */

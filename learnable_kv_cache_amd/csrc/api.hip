@@ -153,7 +153,7 @@ int lte_prefill_score(const lte_config* cfg, int64_t T, const uint16_t* k, const
     WsPtrs w = ws_ptrs(sh, T, workspace);
     hipStream_t st = hipStream_t(stream);
     LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
-    return hip_status(launch_score_prefill(sh, T, k, v, w.w1p, *cnn, w.scores, st));
+    return hip_status(launch_score_prefill(sh, T, nullptr, k, v, w.w1p, *cnn, w.scores, st));
 }
 
 int lte_prefill_select(const lte_config* cfg, int64_t T, const float* score_override,
@@ -174,7 +174,7 @@ int lte_prefill_select(const lte_config* cfg, int64_t T, const float* score_over
         if (e != hipSuccess) return LTE_ERR_HIP;
     }
     return hip_status(
-        launch_select(sh, T, sc, w.rank, w.thr, w.ncand, w.select_scratch, st));
+        launch_select(sh, T, nullptr, sc, w.rank, w.thr, w.ncand, w.select_scratch, st));
 }
 
 int lte_prefill_attend(const lte_config* cfg, int64_t T, const uint16_t* q, const uint16_t* k,
@@ -187,7 +187,7 @@ int lte_prefill_attend(const lte_config* cfg, int64_t T, const uint16_t* q, cons
     LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
     WsPtrs w = ws_ptrs(sh, T, workspace);
     return hip_status(
-        launch_attend_prefill(sh, T, q, k, v, w.rank, w.thr, out, hipStream_t(stream)));
+        launch_attend_prefill(sh, T, nullptr, q, k, v, w.rank, w.thr, out, hipStream_t(stream)));
 }
 
 int lte_prefill_build_cache(const lte_config* cfg, int64_t T, const uint16_t* k,
@@ -199,7 +199,7 @@ int lte_prefill_build_cache(const lte_config* cfg, int64_t T, const uint16_t* k,
     Shape sh = make_shape(*cfg);
     LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
     WsPtrs w = ws_ptrs(sh, T, workspace);
-    return hip_status(launch_build_cache(sh, T, k, v, w.scores, w.rank, w.thr,
+    return hip_status(launch_build_cache(sh, T, nullptr, k, v, w.scores, w.rank, w.thr,
                                          cache_view(sh, cache), hipStream_t(stream)));
 }
 
@@ -218,6 +218,39 @@ int lte_prefill(const lte_config* cfg, int64_t T, const uint16_t* q, const uint1
     LTE_TRY(lte_prefill_attend(cfg, T, q, k, v, workspace, workspace_bytes, out, stream));
     if (cache != nullptr)
         LTE_TRY(lte_prefill_build_cache(cfg, T, k, v, workspace, workspace_bytes, cache, stream));
+    return LTE_OK;
+}
+
+int lte_prefill_varlen(const lte_config* cfg, int64_t T, const int32_t* seq_lens,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const lte_cnn* cnn, const float* score_override, void* cache,
+                       void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {
+    LTE_TRY(check_cfg(cfg));
+    LTE_TRY(check_T(T));
+    if (!seq_lens || !q || !k || !v || !out) return LTE_ERR_INVALID_ARG;
+    if (score_override == nullptr) LTE_TRY(check_cnn(cnn));
+    Shape sh = make_shape(*cfg);
+    LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
+    WsPtrs w = ws_ptrs(sh, T, workspace);
+    hipStream_t st = hipStream_t(stream);
+    const float* sc = w.scores;
+    if (score_override == nullptr) {
+        LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
+        LTE_TRY(hip_status(
+            launch_score_prefill(sh, T, seq_lens, k, v, w.w1p, *cnn, w.scores, st)));
+    } else {
+        hipError_t e = hipMemcpyAsync(w.scores, score_override,
+                                      size_t(sh.B) * sh.Hkv * T * sizeof(float),
+                                      hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return LTE_ERR_HIP;
+    }
+    LTE_TRY(hip_status(
+        launch_select(sh, T, seq_lens, sc, w.rank, w.thr, w.ncand, w.select_scratch, st)));
+    LTE_TRY(hip_status(
+        launch_attend_prefill(sh, T, seq_lens, q, k, v, w.rank, w.thr, out, st)));
+    if (cache != nullptr)
+        LTE_TRY(hip_status(launch_build_cache(sh, T, seq_lens, k, v, w.scores, w.rank, w.thr,
+                                             cache_view(sh, cache), st)));
     return LTE_OK;
 }
 

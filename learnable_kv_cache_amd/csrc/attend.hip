@@ -56,7 +56,8 @@ __device__ __forceinline__ int swz(int r) {
 
 template <int D, int G>
 __global__ __launch_bounds__(512) void attend_prefill_kernel(
-    int T, int Hq, int Hkv, int s, int w, int ntile, const uint16_t* __restrict__ q,
+    int T, int Hq, int Hkv, int s, int w, int ntile, const int32_t* __restrict__ seq_lens,
+    const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ thr,
     uint16_t* __restrict__ out) {
@@ -99,7 +100,9 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const int b = bg / Hkv;
     const int g = bg % Hkv;
     const int i0 = tile * P;
-    const int i_last = min(i0 + P, T) - 1;
+    const int Tb = seq_len_of(seq_lens, b, T);      // this sequence's length
+    if (i0 >= Tb) return;                           // every row of the tile is padding
+    const int i_last = min(i0 + P, Tb) - 1;
     const int band_lo = max(0, i0 - w + 1);
     const int band_hi = i_last;
     const int nband = (band_hi - band_lo + 1 + 63) / 64;
@@ -413,9 +416,9 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
 }
 
 template <int D>
-hipError_t launch_attend_d(const Shape& sh, int64_t T, const uint16_t* q, const uint16_t* k,
-                           const uint16_t* v, const int32_t* rank, const int32_t* thr,
-                           uint16_t* out, hipStream_t st) {
+hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens, const uint16_t* q,
+                           const uint16_t* k, const uint16_t* v, const int32_t* rank,
+                           const int32_t* thr, uint16_t* out, hipStream_t st) {
     const int G = sh.G;
     const int P = 256 / G;
     const int ntile = int((T + P - 1) / P);
@@ -423,7 +426,8 @@ hipError_t launch_attend_d(const Shape& sh, int64_t T, const uint16_t* q, const 
 #define LTE_ATTEND_CASE(GG)                                                                   \
     case GG:                                                                                  \
         hipLaunchKernelGGL((attend_prefill_kernel<D, GG>), grid, dim3(512), 0, st, int(T),    \
-                           sh.Hq, sh.Hkv, sh.s, sh.w, ntile, q, k, v, rank, thr, out);        \
+                           sh.Hq, sh.Hkv, sh.s, sh.w, ntile, seq_lens, q, k, v, rank, thr,   \
+                           out);                                                              \
         break;
     switch (G) {
         LTE_ATTEND_CASE(1)
@@ -440,11 +444,12 @@ hipError_t launch_attend_d(const Shape& sh, int64_t T, const uint16_t* q, const 
 
 }  // namespace
 
-hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const uint16_t* q,
-                                 const uint16_t* k, const uint16_t* v, const int32_t* rank,
-                                 const int32_t* thr, uint16_t* out, hipStream_t st) {
-    if (sh.D == 128) return launch_attend_d<128>(sh, T, q, k, v, rank, thr, out, st);
-    return launch_attend_d<64>(sh, T, q, k, v, rank, thr, out, st);
+hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
+                                 const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* rank, const int32_t* thr, uint16_t* out,
+                                 hipStream_t st) {
+    if (sh.D == 128) return launch_attend_d<128>(sh, T, seq_lens, q, k, v, rank, thr, out, st);
+    return launch_attend_d<64>(sh, T, seq_lens, q, k, v, rank, thr, out, st);
 }
 
 }  // namespace lte

@@ -37,7 +37,8 @@ __global__ void cache_init_kernel(int BG, int w, int s, CacheView c) {
 }
 
 // One workgroup (256 threads) per (batch, KV head): bookkeeping of the cache.
-__global__ __launch_bounds__(256) void cache_meta_kernel(int T, int s, int w, int C,
+__global__ __launch_bounds__(256) void cache_meta_kernel(int Tmax, int Hkv, int s, int w, int C,
+                                                         const int32_t* __restrict__ seq_lens,
                                                          const float* __restrict__ scores,
                                                          const int32_t* __restrict__ rank,
                                                          const int32_t* __restrict__ thr,
@@ -47,8 +48,9 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int T, int s, int w, in
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int bg = blockIdx.x;
-    const float* r = scores + long(bg) * T;
-    const int32_t* rk = rank + long(bg) * T;
+    const int T = seq_len_of(seq_lens, bg / Hkv, Tmax);     // this sequence's length
+    const float* r = scores + long(bg) * Tmax;
+    const int32_t* rk = rank + long(bg) * Tmax;
     const float qnan = __builtin_nanf("");
 
     // ring scores
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int T, int s, int w, in
     const int m = T - 1 - w;
     int len = 0;
     if (m >= 0 && C > 0) {
-        const int th = thr[long(bg) * T + m];
+        const int th = thr[long(bg) * Tmax + m];
         for (int base = s; base <= m; base += 256 * 8) {
             int cnt = 0;
             int ent[8];
@@ -153,8 +155,9 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int T, int s, int w, in
 
 // Copies K/V rows into the cache slots: sink, retained segment, ring.
 // grid.x covers (batch, KV head) x slot groups; one 16-byte chunk per thread.
-__global__ __launch_bounds__(256) void cache_copy_kernel(int T, int Hkv, int D, int s, int w,
+__global__ __launch_bounds__(256) void cache_copy_kernel(int Tmax, int Hkv, int D, int s, int w,
                                                          int C, int S, int slots_per_block,
+                                                         const int32_t* __restrict__ seq_lens,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          CacheView c) {
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(256) void cache_copy_kernel(int T, int Hkv, int D, 
     const int sb = blockIdx.x % nsb;
     const int b = bg / Hkv;
     const int g = bg % Hkv;
+    const int T = seq_len_of(seq_lens, b, Tmax);            // this sequence's length
     const int chunks = D / 8;
     const int cnt = c.count[bg];
     for (int x = threadIdx.x; x < slots_per_block * chunks; x += blockDim.x) {
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(256) void cache_copy_kernel(int T, int Hkv, int D, 
             if (jj >= 0) j = jj;
         }
         if (j < 0) continue;
-        const long src = ((long(b) * T + j) * Hkv + g) * D + ch * 8;
+        const long src = ((long(b) * Tmax + j) * Hkv + g) * D + ch * 8;
         const long dst = (long(bg) * S + slot) * D + ch * 8;
         *reinterpret_cast<uint4*>(c.k + dst) = *reinterpret_cast<const uint4*>(k + src);
         *reinterpret_cast<uint4*>(c.v + dst) = *reinterpret_cast<const uint4*>(v + src);
@@ -199,18 +203,20 @@ hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_build_cache(const Shape& sh, int64_t T, const uint16_t* k, const uint16_t* v,
-                              const float* scores, const int32_t* rank, const int32_t* thr,
-                              const CacheView& cache, hipStream_t st) {
+hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_lens,
+                              const uint16_t* k, const uint16_t* v, const float* scores,
+                              const int32_t* rank, const int32_t* thr, const CacheView& cache,
+                              hipStream_t st) {
     const int BG = sh.B * sh.Hkv;
-    hipLaunchKernelGGL(cache_meta_kernel, dim3(BG), dim3(256), 0, st, int(T), sh.s, sh.w, sh.C,
-                       scores, rank, thr, cache);
+    hipLaunchKernelGGL(cache_meta_kernel, dim3(BG), dim3(256), 0, st, int(T), sh.Hkv, sh.s, sh.w,
+                       sh.C, seq_lens, scores, rank, thr, cache);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int spb = 32;                                  // slots per workgroup
     const int nsb = (sh.S + spb - 1) / spb;
     hipLaunchKernelGGL(cache_copy_kernel, dim3(unsigned(long(BG) * nsb)), dim3(256), 0, st,
-                       int(T), sh.Hkv, sh.D, sh.s, sh.w, sh.C, sh.S, spb, k, v, cache);
+                       int(T), sh.Hkv, sh.D, sh.s, sh.w, sh.C, sh.S, spb, seq_lens, k, v,
+                       cache);
     return hipGetLastError();
 }
 

@@ -30,6 +30,14 @@ constexpr int32_t kAllPass = 0x7ffffffe;   // thr when every candidate is kept
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Length of sequence b of a prefill: seq_lens[b] clamped to [1, T], or T for
+// every sequence when there is no length array.
+__device__ __forceinline__ int seq_len_of(const int32_t* seq_lens, int b, int T) {
+    if (seq_lens == nullptr) return T;
+    const int n = seq_lens[b];
+    return n < 1 ? 1 : (n > T ? T : n);
+}
+
 // Plain copy of lte_config with derived sizes.
 struct Shape {
     int B, Hq, Hkv, D, s, w, C, G, S;   // S = s + C + w cache slots per (b, g)
@@ -169,17 +177,22 @@ inline WsLayout ws_layout(const Shape& sh, int64_t T) {
 // launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
 hipError_t launch_pack_w1(const Shape& sh, const float* w1, uint16_t* w1p, hipStream_t st);
-hipError_t launch_score_prefill(const Shape& sh, int64_t T, const uint16_t* k, const uint16_t* v,
-                                const uint16_t* w1p, const lte_cnn& cnn, float* scores,
-                                hipStream_t st);
-hipError_t launch_select(const Shape& sh, int64_t T, const float* scores, int32_t* rank,
-                         int32_t* thr, int32_t* ncand, uint32_t* scratch, hipStream_t st);
-hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const uint16_t* q,
-                                 const uint16_t* k, const uint16_t* v, const int32_t* rank,
-                                 const int32_t* thr, uint16_t* out, hipStream_t st);
-hipError_t launch_build_cache(const Shape& sh, int64_t T, const uint16_t* k, const uint16_t* v,
-                              const float* scores, const int32_t* rank, const int32_t* thr,
-                              const CacheView& cache, hipStream_t st);
+// Prefill launchers: T is the row count of every [B][T] tensor; seq_lens (device,
+// [B], or null for T everywhere) gives each sequence's length.
+hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
+                                const uint16_t* k, const uint16_t* v, const uint16_t* w1p,
+                                const lte_cnn& cnn, float* scores, hipStream_t st);
+hipError_t launch_select(const Shape& sh, int64_t T, const int32_t* seq_lens, const float* scores,
+                         int32_t* rank, int32_t* thr, int32_t* ncand, uint32_t* scratch,
+                         hipStream_t st);
+hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
+                                 const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* rank, const int32_t* thr, uint16_t* out,
+                                 hipStream_t st);
+hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_lens,
+                              const uint16_t* k, const uint16_t* v, const float* scores,
+                              const int32_t* rank, const int32_t* thr, const CacheView& cache,
+                              hipStream_t st);
 hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_t st);
 hipError_t launch_score_evict(const Shape& sh, const lte_cnn& cnn, const uint16_t* k_t,
                               const uint16_t* v_t, const CacheView& cache, hipStream_t st);

@@ -9,8 +9,9 @@
 // GELU, the 96-term second layer and the sigmoid run in fp32.
 //
 // Grid: one workgroup per 124 consecutive tokens of one (batch, KV head).
-// Tokens outside [0, T) read as zero (first layer's padding) and their hidden
-// activations are zero (second layer's padding).
+// Tokens outside [0, T_b) read as zero (first layer's padding) and their hidden
+// activations are zero (second layer's padding); T_b is the sequence's length
+// (seq_lens[b], or T for every sequence).
 #include "score_core.h"
 
 namespace lte {
@@ -37,7 +38,8 @@ __global__ void pack_w1_kernel(int Hkv, int D, const float* __restrict__ w1,
 
 template <int D>
 __global__ __launch_bounds__(256) void score_prefill_kernel(
-    int T, int Hkv, int ntile, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int T, int Hkv, int ntile, const int32_t* __restrict__ seq_lens,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const bf16x8* __restrict__ w1p, const float* __restrict__ b1, const float* __restrict__ w2,
     const float* __restrict__ b2, float* __restrict__ scores) {
     __shared__ __align__(16) unsigned char buf[ScoreSmem<D>::kBytes];
@@ -50,6 +52,8 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     const int b = bg / Hkv;
     const int g = bg % Hkv;
     const int t0 = tile * kScoreTile;
+    const int Tb = seq_len_of(seq_lens, b, T);
+    if (t0 >= Tb) return;                                    // the whole tile is padding
 
     bf16x8* wl = reinterpret_cast<bf16x8*>(buf);
     const bf16x8* wsrc = w1p + long(g) * NW;
@@ -61,14 +65,14 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     const uint16_t* vb = v + (long(b) * T * Hkv + g) * D;
     float* out = scores + long(bg) * T;
     score_chunk<D>(
-        buf, w2s, b1 + g * kHidden, b2[g], t0, 0, T - 1,
+        buf, w2s, b1 + g * kHidden, b2[g], t0, 0, Tb - 1,
         [&](int x, const uint16_t*& kp, const uint16_t*& vp) {
-            if (x < 0 || x >= T) return false;
+            if (x < 0 || x >= Tb) return false;
             kp = kb + long(x) * row_stride;
             vp = vb + long(x) * row_stride;
             return true;
         },
-        [&](int x) { return x < 0 || x >= T; },
+        [&](int x) { return x < 0 || x >= Tb; },
         [&](int t, float r) { out[t] = r; });
 }
 
@@ -83,18 +87,18 @@ hipError_t launch_pack_w1(const Shape& sh, const float* w1, uint16_t* w1p, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_score_prefill(const Shape& sh, int64_t T, const uint16_t* k, const uint16_t* v,
-                                const uint16_t* w1p, const lte_cnn& cnn, float* scores,
-                                hipStream_t st) {
+hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
+                                const uint16_t* k, const uint16_t* v, const uint16_t* w1p,
+                                const lte_cnn& cnn, float* scores, hipStream_t st) {
     const int ntile = int((T + kScoreTile - 1) / kScoreTile);
     dim3 grid(unsigned(long(sh.B) * sh.Hkv * ntile));
     const bf16x8* wp = reinterpret_cast<const bf16x8*>(w1p);
     if (sh.D == 128) {
         hipLaunchKernelGGL(score_prefill_kernel<128>, grid, dim3(256), 0, st, int(T), sh.Hkv,
-                           ntile, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+                           ntile, seq_lens, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
     } else {
         hipLaunchKernelGGL(score_prefill_kernel<64>, grid, dim3(256), 0, st, int(T), sh.Hkv,
-                           ntile, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+                           ntile, seq_lens, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
     }
     return hipGetLastError();
 }

@@ -61,8 +61,9 @@ __device__ __forceinline__ int block_excl_scan(int x, int* wsum, int* total) {
 
 template <int ELEMS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    int T, int s, int w, int C, int rbs, int nsnap_max, long scratch_words,
-    const float* __restrict__ scores, int32_t* __restrict__ rank_out,
+    int T, int Hkv, int s, int w, int C, int rbs, int nsnap_max, long scratch_words,
+    const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
+    int32_t* __restrict__ rank_out,
     int32_t* __restrict__ thr_out, int32_t* __restrict__ ncand_out,
     uint32_t* __restrict__ scratch) {
     __shared__ int wsum[kSelWaves];
@@ -90,7 +91,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t* pre = bm + long(nsnap_max) * W;        // [nsnap][W]
 
     // ---- 1. candidates in index order -------------------------------------
-    const int last_leaving = T - 1 - w;              // last token that leaves the window
+    const int Tb = seq_len_of(seq_lens, bg / Hkv, T);    // this sequence's length
+    const int last_leaving = Tb - 1 - w;             // last token that leaves the window
     int n = 0;
     for (int base = 0; base < T; base += kSelThreads) {
         const int j = base + tid;
@@ -322,18 +324,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 }  // namespace
 
-hipError_t launch_select(const Shape& sh, int64_t T, const float* scores, int32_t* rank,
-                         int32_t* thr, int32_t* ncand, uint32_t* scratch, hipStream_t st) {
+hipError_t launch_select(const Shape& sh, int64_t T, const int32_t* seq_lens, const float* scores,
+                         int32_t* rank, int32_t* thr, int32_t* ncand, uint32_t* scratch,
+                         hipStream_t st) {
     const int rbs = select_rbs(T);
     const int nsnap_max = int(select_nsnap_max(T));
     const long words = long(select_scratch_words(T));
     dim3 grid(unsigned(sh.B * sh.Hkv));
     if (T <= 4 * kSelThreads) {
-        hipLaunchKernelGGL(select_kernel<4>, grid, dim3(kSelThreads), 0, st, int(T), sh.s, sh.w,
-                           sh.C, rbs, nsnap_max, words, scores, rank, thr, ncand, scratch);
+        hipLaunchKernelGGL(select_kernel<4>, grid, dim3(kSelThreads), 0, st, int(T), sh.Hkv,
+                           sh.s, sh.w, sh.C, rbs, nsnap_max, words, seq_lens, scores, rank, thr,
+                           ncand, scratch);
     } else {
-        hipLaunchKernelGGL(select_kernel<32>, grid, dim3(kSelThreads), 0, st, int(T), sh.s, sh.w,
-                           sh.C, rbs, nsnap_max, words, scores, rank, thr, ncand, scratch);
+        hipLaunchKernelGGL(select_kernel<32>, grid, dim3(kSelThreads), 0, st, int(T), sh.Hkv,
+                           sh.s, sh.w, sh.C, rbs, nsnap_max, words, seq_lens, scores, rank, thr,
+                           ncand, scratch);
     }
     return hipGetLastError();
 }

@@ -65,6 +65,8 @@ SIGNATURES = {
     "lte_workspace_get_layout": (ctypes.c_int, [_CFG, _I64, ctypes.POINTER(_WsLayout)]),
     "lte_cache_init": (ctypes.c_int, [_CFG, _P, _P]),
     "lte_prefill": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _CNNP, _P, _P, _P, _SZ, _P, _P]),
+    "lte_prefill_varlen": (ctypes.c_int,
+                           [_CFG, _I64, _P, _P, _P, _P, _CNNP, _P, _P, _P, _SZ, _P, _P]),
     "lte_prefill_score": (ctypes.c_int, [_CFG, _I64, _P, _P, _CNNP, _P, _SZ, _P]),
     "lte_prefill_select": (ctypes.c_int, [_CFG, _I64, _P, _P, _SZ, _P]),
     "lte_prefill_attend": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _P, _SZ, _P, _P]),
@@ -182,7 +184,9 @@ class Layer:
 
     # -- prefill -------------------------------------------------------------------
     def prefill(self, q, k, v, cnn: CNN | None = None, score_override=None, cache=None,
-                workspace=None, out=None):
+                workspace=None, out=None, seq_lens=None):
+        """Prefill of [B, T] prompts; seq_lens (int32 [B] on the device) gives each
+        sequence's length when they differ (rows at or past it are padding)."""
         c = self.cfg
         B, T = q.shape[0], q.shape[1]
         _need(q, torch.bfloat16, (c.batch, T, c.q_heads, c.head_dim), "q")
@@ -194,11 +198,18 @@ class Layer:
             workspace = self.alloc_workspace(T, q.device)
         if out is None:
             out = torch.empty_like(q)
-        _check(lib().lte_prefill(
-            ctypes.byref(self._c), int(T), _ptr(q), _ptr(k), _ptr(v),
-            ctypes.byref(cnn.c) if cnn is not None else None, _ptr(score_override),
-            _ptr(cache), _ptr(workspace), int(workspace.numel()), _ptr(out), _stream()),
-            "lte_prefill")
+        cnn_p = ctypes.byref(cnn.c) if cnn is not None else None
+        if seq_lens is None:
+            _check(lib().lte_prefill(
+                ctypes.byref(self._c), int(T), _ptr(q), _ptr(k), _ptr(v), cnn_p,
+                _ptr(score_override), _ptr(cache), _ptr(workspace), int(workspace.numel()),
+                _ptr(out), _stream()), "lte_prefill")
+        else:
+            _need(seq_lens, torch.int32, (c.batch,), "seq_lens")
+            _check(lib().lte_prefill_varlen(
+                ctypes.byref(self._c), int(T), _ptr(seq_lens), _ptr(q), _ptr(k), _ptr(v), cnn_p,
+                _ptr(score_override), _ptr(cache), _ptr(workspace), int(workspace.numel()),
+                _ptr(out), _stream()), "lte_prefill_varlen")
         return out
 
     def prefill_score(self, k, v, cnn: CNN, workspace):

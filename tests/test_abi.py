@@ -81,6 +81,13 @@ def test_calls_fail_before_launch_on_bad_arguments():
     assert L.lte_prefill(cfg, T, fake, fake, fake, None, None, None, fake, ws, fake, None) == 1
     # workspace too small
     assert L.lte_prefill(cfg, T, fake, fake, fake, None, fake, None, fake, ws - 1, fake, None) == 5
+    # ragged prefill: null lengths, then the same checks as the equal-length call
+    VL = L.lte_prefill_varlen
+    assert VL(cfg, T, None, fake, fake, fake, None, fake, None, fake, ws, fake, None) == 1
+    assert VL(cfg, T, fake, None, fake, fake, None, fake, None, fake, ws, fake, None) == 1
+    assert VL(cfg, 40000, fake, fake, fake, fake, None, fake, None, fake, ws, fake, None) == 2
+    assert VL(cfg, T, fake, fake, fake, fake, None, None, None, fake, ws, fake, None) == 1
+    assert VL(cfg, T, fake, fake, fake, fake, None, fake, None, fake, ws - 1, fake, None) == 5
     # decode: null cache, small workspace, CNN with a null member
     assert L.lte_decode_attend(cfg, fake, None, fake, 1 << 30, fake, None) == 1
     assert L.lte_decode_attend(cfg, fake, fake, fake, 16, fake, None) == 5
