@@ -14,9 +14,14 @@
 //     gathered columns below the band (sink + retained tokens alive at the
 //     tile's first row, via the per-head rank/thr lists), which are listed
 //     while the first band block loads.
-//   * K/V tiles are double-buffered in LDS and filled by direct global->LDS
-//     loads issued one block ahead, so one barrier per block suffices; the
-//     two waves sharing a SIMD then alternate between MFMA and softmax work.
+//   * K/V tiles are double-buffered in LDS: the first by direct global->LDS
+//     loads, later ones fetched into registers one block ahead and stored to
+//     the free buffer at the end of the block, so one barrier per block
+//     suffices (with a direct load in flight the compiler would wait for all
+//     outstanding LDS reads before using any).  Scheduling groups keep three
+//     k-steps of K operands and four V operands in flight ahead of the MFMAs.
+//   * waves 0-3 hold a higher issue priority during q.k, so the two waves of a
+//     SIMD drift apart: one's softmax runs beside the other's MFMA work.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows from LDS are the A
 //     operand, each wave's 32 query rows stay in registers as the B operand.
 //     A lane then owns one query row, so the row max/sum of the online
@@ -25,8 +30,9 @@
 //     to bf16).  V stays row-major in LDS; its MFMA operand (8 keys of one
 //     dim per lane) is read with ds_read_b64_tr_b16, whose 16-lane transpose
 //     turns four 4-dim row pieces into four keys of one dim per lane.
-//   * K and V tiles sit in LDS as 16-byte chunks XOR-swizzled by row, so the
-//     row-strided MFMA operand reads hit distinct banks.
+//   * K and V tiles sit in LDS as 16-byte chunks XOR-swizzled by row (each
+//     tensor its own pattern), so the row-strided MFMA operand reads hit
+//     distinct banks.
 //   * fp32 online softmax on raw logits, the 1/sqrt(D) scale and log2(e)
 //     folded into one FMA before exp2; masked keys are -inf; the reference
 //     maximum of a row moves only when exceeded by more than 2^8 in the
@@ -52,6 +58,19 @@ template <int D>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (D == 128) return (((r & 1) * 10) | ((r & 2) << 1)) ^ ((r >> 2) & 3);
     else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
+
+// LDS chunk swizzle of V tile row r.  The transposing V read takes, for one
+// output tile of 32 dims, 4 consecutive keys x 64 bytes per 32 lanes; XOR-ing
+// bits 2-3 of the chunk index with the key's position in its group of 4 (D =
+// 128: 256-byte rows) or bit 1 of the key (D = 64: 128-byte rows, two per
+// 256-byte bank line) puts those 4 key pieces in different 64-byte bank
+// quarters, and leaves a lane's read address affine in the key and in the
+// dim tile but for one XOR of the tile index.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    if constexpr (D == 128) return (r & 3) << 2;
+    else return ((r >> 1) & 1) << 2;
 }
 
 template <int D, int G>
@@ -126,20 +145,48 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
             const int xi = wave * LPW + x;                                                 \
             const int c = xi * 64 + lane;                                                  \
             const int trow = c / CPR;                                                      \
-            const int gch = (c % CPR) ^ swz<D>(trow);                                      \
             int row;                                                                       \
             if (fb < nband) row = min(band_lo + fb * 64 + trow, band_hi);                  \
             else row = int(lst[min((fb - nband) * 64 + trow, kMaxList - 1)] & 0xffffu);    \
-            const uint32_t off = __umul24(uint32_t(row), kv_bytes) + uint32_t(gch * 16);   \
+            const uint32_t roff = __umul24(uint32_t(row), kv_bytes);                       \
+            const uint32_t koff = roff + uint32_t(((c % CPR) ^ swz<D>(trow)) * 16);       \
+            const uint32_t voff = roff + uint32_t(((c % CPR) ^ vswz<D>(trow)) * 16);      \
             __builtin_amdgcn_global_load_lds(                                              \
-                (const __attribute__((address_space(1))) void*)(kbytes + off),             \
+                (const __attribute__((address_space(1))) void*)(kbytes + koff),            \
                 (__attribute__((address_space(3))) void*)(&KB[xi * 64]), 16, 0, 0);         \
             __builtin_amdgcn_global_load_lds(                                              \
-                (const __attribute__((address_space(1))) void*)(vbytes + off),             \
+                (const __attribute__((address_space(1))) void*)(vbytes + voff),            \
                 (__attribute__((address_space(3))) void*)(&VB[xi * 64]), 16, 0, 0);         \
         }                                                                                  \
     }
     LTE_ISSUE(0, K0, V0)                          // first band block: needs no list
+    // Blocks after the first are staged through registers instead: with a
+    // direct-to-LDS load outstanding the compiler waits for every LDS read in
+    // flight before using any, which serialises the operand reads of the MFMAs.
+    u32x4 kst[LPW], vst[LPW];
+#define LTE_FETCH(BLK)                                                                      \
+    {                                                                                      \
+        const int fb = (BLK);                                                              \
+        _Pragma("unroll") for (int x = 0; x < LPW; ++x) {                                  \
+            const int c = (wave * LPW + x) * 64 + lane;                                    \
+            const int trow = c / CPR;                                                      \
+            int row;                                                                       \
+            if (fb < nband) row = min(band_lo + fb * 64 + trow, band_hi);                  \
+            else row = int(lst[min((fb - nband) * 64 + trow, kMaxList - 1)] & 0xffffu);    \
+            const uint32_t roff = __umul24(uint32_t(row), kv_bytes);                       \
+            kst[x] = *reinterpret_cast<const u32x4*>(                                      \
+                kbytes + roff + uint32_t(((c % CPR) ^ swz<D>(trow)) * 16));                \
+            vst[x] = *reinterpret_cast<const u32x4*>(                                      \
+                vbytes + roff + uint32_t(((c % CPR) ^ vswz<D>(trow)) * 16));               \
+        }                                                                                  \
+    }
+#define LTE_STORE(KB, VB)                                                                   \
+    {                                                                                      \
+        _Pragma("unroll") for (int x = 0; x < LPW; ++x) {                                  \
+            KB[(wave * LPW + x) * 64 + lane] = kst[x];                                     \
+            VB[(wave * LPW + x) * 64 + lane] = vst[x];                                     \
+        }                                                                                  \
+    }
 
     // ranks of the first kBr band keys: a band key j can be a retained column
     // of a row of the tile only if j <= i_last - w <= band_lo + P - 2
@@ -235,14 +282,26 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     __builtin_amdgcn_s_waitcnt(0);                // this wave's loads of block 0 landed
     __syncthreads();                              // everyone's, and lfull, brank
 
+    uint32_t vrd[DT];           // this lane's byte offsets of its V operand pieces
+    {
+        const int grp = lane >> 4;
+        const int i = lane & 15;
+        const int key0 = 4 * (grp >> 1) + (i >> 2);
+        const int c_lo = 2 * (grp & 1) + ((i & 3) >> 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            vrd[dt] = uint32_t(key0 * CPR * 16 + ((4 * dt + c_lo) ^ vswz<D>(key0)) * 16 + 8 * (i & 1));
+    }
+
     // one block: issue the next block's loads into (KN, VN), compute on (KC, VC)
     auto step = [&](const int blk, u32x4* KC, u32x4* VC, u32x4* KN, u32x4* VN) {
-        if (blk + 1 < nblk) LTE_ISSUE(blk + 1, KN, VN)     // in flight during this block
+        if (blk + 1 < nblk) LTE_FETCH(blk + 1)             // in flight during this block
         const bool is_list = blk >= nband;
         const int lb = blk - nband;                        // list block index
         const int jb0 = band_lo + blk * 64;                // first key of a band block
 
         // ---- S^T = K Q^T for 64 keys x this wave's 32 rows -----------------------
+        if (wave < NW / 2) __builtin_amdgcn_s_setprio(2);
         f32x16 sacc[2];
         sacc[0] = f32x16{};
         sacc[1] = f32x16{};
@@ -256,6 +315,16 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
                 sacc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[ks], 0, 0, 0);
             }
         }
+        // schedule: the K operands of the next three k-steps are in flight while
+        // this one's MFMAs run
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+        for (int x = 0; x < KK - 3; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
+        __builtin_amdgcn_s_setprio(0);
         // ---- mask in place: element e of subtile ks is key slot
         //      ks*32 + (e/4)*8 + half*4 + e%4 of this block ----------------------------
         const bool list_full =
@@ -361,7 +430,9 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         // ---- O^T += V^T P^T ------------------------------------------------------
         // operand element e of lane (16-group G, index i) is V[key][dt*32 + (G&1)*16 + i]
         // with key = cc*16 + (e<4 ? 4h + e : 8 + 4h + e-4), h = lane/32: two
-        // transposing reads, each of 4 keys, from rows that lane i of the group names
+        // transposing reads, each of 4 keys, from rows that lane i of the group
+        // names, at byte vrd[dt] + (cc*16 + 8r) * row bytes of the tile
+        const char* vb = reinterpret_cast<const char*>(VC);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -369,16 +440,10 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
                 bf16x8 a;
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const int grp = lane >> 4;
-                    const int i = lane & 15;
-                    const int key = cc * 16 + 8 * r + 4 * (grp >> 1) + (i >> 2);
-                    const int d0 = dt * 32 + (grp & 1) * 16 + 4 * (i & 3);
-                    const int chunk = (d0 >> 3) ^ swz<D>(key);
-                    const __bf16* src =
-                        reinterpret_cast<const __bf16*>(&VC[key * CPR + chunk]) + (d0 & 7);
                     typedef short v4i16 __attribute__((ext_vector_type(4)));
                     const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4i16*)(src));
+                        (__attribute__((address_space(3))) v4i16*)(vb + vrd[dt] +
+                                                                   (cc * 16 + 8 * r) * CPR * 16));
                     const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
                     a[4 * r + 0] = b4[0];
                     a[4 * r + 1] = b4[1];
@@ -388,14 +453,24 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
                 acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[cc], acc_o[dt], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);            // this wave's loads of the next block landed
-        __syncthreads();                          // everyone's; and the current tiles are free
+        // schedule: four V operands in flight ahead of the MFMA that takes them
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
+#pragma unroll
+        for (int x = 0; x < 4 * DT - 4; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
+        if (blk + 1 < nblk) LTE_STORE(KN, VN)     // the other buffers: free since the last barrier
+        __syncthreads();                          // everyone's stores; and the current tiles are free
     };
     for (int blk = 0; blk < nblk; blk += 2) {
         step(blk, K0, V0, K1, V1);
         if (blk + 1 < nblk) step(blk + 1, K1, V1, K0, V0);
     }
 #undef LTE_ISSUE
+#undef LTE_FETCH
+#undef LTE_STORE
 
     // ---- normalise and store: element e of d-tile dt is dim dt*32 + (e/4)*8 + half*4 + e%4
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
