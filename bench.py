@@ -14,11 +14,12 @@ this host.
 
 Beside it, the same engine as the two comparators of the LTE paper's Figure 4
 (sink + sliding-window attention with no retained segment, and full causal
-attention as a window covering the whole sequence), timed on the same inputs.
+attention as a window covering the whole sequence), timed on the same inputs,
+and a chunked prefill of the next 512 tokens onto the prompt's cache.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
                        [--no-cpu-baseline] [--no-decode] [--no-comparators]
-                       [--copy-calibration MIB]
+                       [--no-chunk] [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -52,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="sequences the oracle runs for the CPU baseline (0: one per core)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -454,6 +456,28 @@ def main():
                              "decode_step", os.path.join(ROOT, "learnable_kv_cache_amd", "csrc",
                                                          "decode.hip"))},
         }
+    if not args.no_chunk and ndec > 0:
+        # chunked prefill: the prompt's cache extended by the next n tokens in one call
+        n = min(512, ndec)
+        prefill_staged()
+        torch.cuda.synchronize()
+        qc, kc, vc = (x[:, T:T + n].contiguous() for x in (q, k, v))
+        cws = layer.alloc_chunk_workspace(n, dev)
+        cout = torch.empty_like(qc)
+        times = []
+        for _ in range(6):
+            c = cache0.clone()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            layer.prefill_chunk(qc, kc, vc, cnn, c, cws, cout)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+            del c
+        ch_ms = float(np.median(times[1:]))
+        result["chunk"] = {"n": n, "onto_position": T, "ms": ch_ms,
+                           "tokens_per_s": B * n / (ch_ms * 1e-3)}
+        del cws, cout
     if not args.no_comparators and not args.no_decode:
         cmp = comparators(inp, wl, T, dev, ndec=min(64, ndec))
         cmp["lte"] = {"window": wl.window, "capacity": wl.capacity, "prefill_attend_ms": att_ms,

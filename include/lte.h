@@ -197,6 +197,32 @@ int lte_prefill_varlen(const lte_config* cfg, int64_t T, const int32_t* seq_lens
                        void* cache, void* workspace, size_t workspace_bytes,
                        uint16_t* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Chunked prefill: n new tokens per sequence appended to a cache at any
+ * position (after a prefill, decode steps or earlier chunks), their outputs
+ * computed, the cache advanced to pos + n.  The result is that of one prefill
+ * over the whole history (up to rounding), because the cache's segment is the
+ * top-C of every candidate that left the window and top-C under the strict
+ * order (score desc, index asc) continues over a union (Figure 2 caption of
+ * the learnable-eviction paper: decisions from scores at window exit, at most
+ * C kept).  Tokens still unscored in the ring get their scores now, those at
+ * the chunk's end keep provisional ones (next_unscored = max(pos + n - 2, s)).
+ *   q   bf16 [B][n][Hq][D];  k, v bf16 [B][n][Hkv][D]: the new tokens
+ *   cnn scoring-CNN parameters (required)
+ *   cache  lte_cache_bytes(cfg) bytes in any state reached by this library
+ *   workspace  lte_chunk_workspace_bytes(cfg, n) bytes; its first
+ *       lte_workspace_bytes(cfg, s + C + w + n) bytes hold the views of
+ *       lte_workspace_get_layout for T = s + C + w + n over the call's
+ *       extended sequence (sink, segment sorted by token, ring, chunk)
+ *   out bf16 [B][n][Hq][D]
+ * Sequences may stand at different positions.  s + C + w + n <= 32768.
+ * ------------------------------------------------------------------------- */
+size_t lte_chunk_workspace_bytes(const lte_config* cfg, int64_t n);
+int lte_prefill_chunk(const lte_config* cfg, int64_t n,
+                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const lte_cnn* cnn, void* cache, void* workspace,
+                      size_t workspace_bytes, uint16_t* out, void* stream);
+
 /* The four stages lte_prefill runs, in order, exposed for timing and tests.
  * Each reads and writes the workspace views described above. */
 int lte_prefill_score(const lte_config* cfg, int64_t T, const uint16_t* k, const uint16_t* v,

@@ -78,6 +78,34 @@ float* dec_part_ptr(const Shape& sh, void* ws) {
     return reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(sh, 0).dec_part);
 }
 
+// Workspace of a chunk of n tokens: a prefill workspace for the extended
+// sequence's Emax = s + C + w + n rows first (so its views read as usual), then
+// the extended K/V and the chunk's per-sequence data.
+struct ChunkLayout {
+    int64_t Emax;
+    size_t ek, ev, ext_len, q_lo, tok_off, warm, score_lo, seg_tok, seg_slot, seg_row, total;
+};
+
+ChunkLayout chunk_layout(const Shape& sh, int64_t n) {
+    ChunkLayout L{};
+    L.Emax = int64_t(sh.s) + sh.C + sh.w + n;
+    const size_t B = size_t(sh.B), BG = B * sh.Hkv;
+    size_t off = ws_layout(sh, L.Emax).total;
+    const size_t kv = B * size_t(L.Emax) * sh.Hkv * sh.D * 2;
+    L.ek = off; off = align256(off + kv);
+    L.ev = off; off = align256(off + kv);
+    L.ext_len = off; off = align256(off + B * 4);
+    L.q_lo = off; off = align256(off + B * 4);
+    L.tok_off = off; off = align256(off + B * 4);
+    L.warm = off; off = align256(off + B * 4);
+    L.score_lo = off; off = align256(off + BG * 4);
+    L.seg_tok = off; off = align256(off + BG * size_t(sh.C) * 4);
+    L.seg_slot = off; off = align256(off + BG * size_t(sh.C) * 4);
+    L.seg_row = off; off = align256(off + BG * size_t(sh.C) * 4);
+    L.total = off;
+    return L;
+}
+
 #define LTE_TRY(expr)                 \
     do {                              \
         int _st = (expr);             \
@@ -153,7 +181,8 @@ int lte_prefill_score(const lte_config* cfg, int64_t T, const uint16_t* k, const
     WsPtrs w = ws_ptrs(sh, T, workspace);
     hipStream_t st = hipStream_t(stream);
     LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
-    return hip_status(launch_score_prefill(sh, T, nullptr, k, v, w.w1p, *cnn, w.scores, st));
+    return hip_status(
+        launch_score_prefill(sh, T, nullptr, nullptr, k, v, w.w1p, *cnn, w.scores, st));
 }
 
 int lte_prefill_select(const lte_config* cfg, int64_t T, const float* score_override,
@@ -187,7 +216,8 @@ int lte_prefill_attend(const lte_config* cfg, int64_t T, const uint16_t* q, cons
     LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
     WsPtrs w = ws_ptrs(sh, T, workspace);
     return hip_status(
-        launch_attend_prefill(sh, T, nullptr, q, k, v, w.rank, w.thr, out, hipStream_t(stream)));
+        launch_attend_prefill(sh, T, nullptr, nullptr, 0, q, k, v, w.rank, w.thr, out,
+                              hipStream_t(stream)));
 }
 
 int lte_prefill_build_cache(const lte_config* cfg, int64_t T, const uint16_t* k,
@@ -199,7 +229,7 @@ int lte_prefill_build_cache(const lte_config* cfg, int64_t T, const uint16_t* k,
     Shape sh = make_shape(*cfg);
     LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
     WsPtrs w = ws_ptrs(sh, T, workspace);
-    return hip_status(launch_build_cache(sh, T, nullptr, k, v, w.scores, w.rank, w.thr,
+    return hip_status(launch_build_cache(sh, T, nullptr, nullptr, k, v, w.scores, w.rank, w.thr,
                                          cache_view(sh, cache), hipStream_t(stream)));
 }
 
@@ -237,7 +267,7 @@ int lte_prefill_varlen(const lte_config* cfg, int64_t T, const int32_t* seq_lens
     if (score_override == nullptr) {
         LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
         LTE_TRY(hip_status(
-            launch_score_prefill(sh, T, seq_lens, k, v, w.w1p, *cnn, w.scores, st)));
+            launch_score_prefill(sh, T, seq_lens, nullptr, k, v, w.w1p, *cnn, w.scores, st)));
     } else {
         hipError_t e = hipMemcpyAsync(w.scores, score_override,
                                       size_t(sh.B) * sh.Hkv * T * sizeof(float),
@@ -247,11 +277,57 @@ int lte_prefill_varlen(const lte_config* cfg, int64_t T, const int32_t* seq_lens
     LTE_TRY(hip_status(
         launch_select(sh, T, seq_lens, sc, w.rank, w.thr, w.ncand, w.select_scratch, st)));
     LTE_TRY(hip_status(
-        launch_attend_prefill(sh, T, seq_lens, q, k, v, w.rank, w.thr, out, st)));
+        launch_attend_prefill(sh, T, seq_lens, nullptr, 0, q, k, v, w.rank, w.thr, out, st)));
     if (cache != nullptr)
-        LTE_TRY(hip_status(launch_build_cache(sh, T, seq_lens, k, v, w.scores, w.rank, w.thr,
+        LTE_TRY(hip_status(launch_build_cache(sh, T, seq_lens, nullptr, k, v, w.scores, w.rank, w.thr,
                                              cache_view(sh, cache), st)));
     return LTE_OK;
+}
+
+size_t lte_chunk_workspace_bytes(const lte_config* cfg, int64_t n) {
+    if (check_cfg(cfg) != LTE_OK) return 0;
+    const Shape sh = make_shape(*cfg);
+    if (n < 1 || int64_t(sh.s) + sh.C + sh.w + n > kMaxT) return 0;
+    return chunk_layout(sh, n).total;
+}
+
+int lte_prefill_chunk(const lte_config* cfg, int64_t n, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const lte_cnn* cnn, void* cache, void* workspace,
+                      size_t workspace_bytes, uint16_t* out, void* stream) {
+    LTE_TRY(check_cfg(cfg));
+    if (n < 1) return LTE_ERR_INVALID_ARG;
+    if (!q || !k || !v || !cache || !out || !workspace) return LTE_ERR_INVALID_ARG;
+    LTE_TRY(check_cnn(cnn));
+    const Shape sh = make_shape(*cfg);
+    if (int64_t(sh.s) + sh.C + sh.w + n > kMaxT) return LTE_ERR_UNSUPPORTED;
+    const ChunkLayout L = chunk_layout(sh, n);
+    if (workspace_bytes < L.total) return LTE_ERR_WORKSPACE;
+    const int64_t E = L.Emax;
+    char* p = static_cast<char*>(workspace);
+    WsPtrs w = ws_ptrs(sh, E, workspace);
+    ChunkView x;
+    x.ext_len = reinterpret_cast<int32_t*>(p + L.ext_len);
+    x.q_lo = reinterpret_cast<int32_t*>(p + L.q_lo);
+    x.tok_off = reinterpret_cast<int32_t*>(p + L.tok_off);
+    x.warm = reinterpret_cast<int32_t*>(p + L.warm);
+    x.score_lo = reinterpret_cast<int32_t*>(p + L.score_lo);
+    x.seg_tok = reinterpret_cast<int32_t*>(p + L.seg_tok);
+    x.seg_slot = reinterpret_cast<int32_t*>(p + L.seg_slot);
+    x.seg_row = reinterpret_cast<int32_t*>(p + L.seg_row);
+    uint16_t* ek = reinterpret_cast<uint16_t*>(p + L.ek);
+    uint16_t* ev = reinterpret_cast<uint16_t*>(p + L.ev);
+    const CacheView c = cache_view(sh, cache);
+    hipStream_t st = hipStream_t(stream);
+    LTE_TRY(hip_status(launch_chunk_gather(sh, int(n), int(E), k, v, c, x, w.scores, ek, ev, st)));
+    LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
+    LTE_TRY(hip_status(
+        launch_score_prefill(sh, E, x.ext_len, x.score_lo, ek, ev, w.w1p, *cnn, w.scores, st)));
+    LTE_TRY(hip_status(
+        launch_select(sh, E, x.ext_len, w.scores, w.rank, w.thr, w.ncand, w.select_scratch, st)));
+    LTE_TRY(hip_status(launch_attend_prefill(sh, E, x.ext_len, x.q_lo, int(n), q, ek, ev, w.rank,
+                                             w.thr, out, st)));
+    return hip_status(
+        launch_build_cache(sh, E, x.ext_len, &x, ek, ev, w.scores, w.rank, w.thr, c, st));
 }
 
 int lte_score_evict(const lte_config* cfg, const lte_cnn* cnn, const uint16_t* k_t,

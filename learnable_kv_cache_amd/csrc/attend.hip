@@ -76,7 +76,7 @@ __device__ __forceinline__ int vswz(int r) {
 template <int D, int G>
 __global__ __launch_bounds__(512) void attend_prefill_kernel(
     int T, int Hq, int Hkv, int s, int w, int ntile, const int32_t* __restrict__ seq_lens,
-    const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ q_lo, int q_rows, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ thr,
     uint16_t* __restrict__ out) {
@@ -122,6 +122,11 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const int Tb = seq_len_of(seq_lens, b, T);      // this sequence's length
     if (i0 >= Tb) return;                           // every row of the tile is padding
     const int i_last = min(i0 + P, Tb) - 1;
+    // with q_lo, only rows >= q_lo[b] are queries: q and out then hold q_rows rows
+    // per sequence, row i at i - q_lo[b]
+    const int qlo = q_lo ? q_lo[b] : 0;
+    if (i_last < qlo) return;
+    const long qrows = q_lo ? long(q_rows) : long(T);
     const int band_lo = max(0, i0 - w + 1);
     const int band_hi = i_last;
     const int nband = (band_hi - band_lo + 1 + 63) / 64;
@@ -200,12 +205,12 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const int p_row = rtile / G;
     const int hh = rtile % G;
     const int i_row = i0 + p_row;
-    const bool row_ok = i_row <= i_last;
-    const int irow = row_ok ? i_row : i_last;
+    const bool row_ok = i_row <= i_last && i_row >= qlo;
+    const int irow = i_row <= i_last ? i_row : i_last;
     const int h = g * G + hh;
     bf16x8 qf[KK];
     {
-        const uint16_t* qrow = q + ((long(b) * T + irow) * Hq + h) * D;
+        const uint16_t* qrow = q + ((long(b) * qrows + max(irow - qlo, 0)) * Hq + h) * D;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
             qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + half * 8);
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (row_ok) {
         const float inv = 1.0f / l_tot;
-        uint16_t* orow = out + ((long(b) * T + i_row) * Hq + h) * D;
+        uint16_t* orow = out + ((long(b) * qrows + (i_row - qlo)) * Hq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -491,9 +496,10 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
 }
 
 template <int D>
-hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens, const uint16_t* q,
-                           const uint16_t* k, const uint16_t* v, const int32_t* rank,
-                           const int32_t* thr, uint16_t* out, hipStream_t st) {
+hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens,
+                           const int32_t* q_lo, int q_rows, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const int32_t* rank, const int32_t* thr,
+                           uint16_t* out, hipStream_t st) {
     const int G = sh.G;
     const int P = 256 / G;
     const int ntile = int((T + P - 1) / P);
@@ -501,7 +507,8 @@ hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens, 
 #define LTE_ATTEND_CASE(GG)                                                                   \
     case GG:                                                                                  \
         hipLaunchKernelGGL((attend_prefill_kernel<D, GG>), grid, dim3(512), 0, st, int(T),    \
-                           sh.Hq, sh.Hkv, sh.s, sh.w, ntile, seq_lens, q, k, v, rank, thr,   \
+                           sh.Hq, sh.Hkv, sh.s, sh.w, ntile, seq_lens, q_lo, q_rows, q, k, v, \
+                           rank, thr,                                                        \
                            out);                                                              \
         break;
     switch (G) {
@@ -520,11 +527,12 @@ hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens, 
 }  // namespace
 
 hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
-                                 const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                 const int32_t* rank, const int32_t* thr, uint16_t* out,
-                                 hipStream_t st) {
-    if (sh.D == 128) return launch_attend_d<128>(sh, T, seq_lens, q, k, v, rank, thr, out, st);
-    return launch_attend_d<64>(sh, T, seq_lens, q, k, v, rank, thr, out, st);
+                                 const int32_t* q_lo, int q_rows, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, const int32_t* rank,
+                                 const int32_t* thr, uint16_t* out, hipStream_t st) {
+    if (sh.D == 128)
+        return launch_attend_d<128>(sh, T, seq_lens, q_lo, q_rows, q, k, v, rank, thr, out, st);
+    return launch_attend_d<64>(sh, T, seq_lens, q_lo, q_rows, q, k, v, rank, thr, out, st);
 }
 
 }  // namespace lte

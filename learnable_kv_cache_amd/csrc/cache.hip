@@ -12,6 +12,11 @@
 // retained set R_{T-1} compacted in token order, the last min(w, T) tokens in
 // the ring, the scores of ring tokens whose right neighbours exist (j <= T-3),
 // pos = T and next_unscored = max(T-2, s).
+//
+// After a chunked prefill the rows are those of the extended sequence (see
+// chunk.hip) and the kernels map them to tokens: row e is token e, or, past
+// the sink of a cache that had lost tokens from its window, the segment's
+// sorted token e - s (rows [s, s + C)) or token e + off (later rows).
 #include "lte_internal.h"
 
 namespace lte {
@@ -39,6 +44,7 @@ __global__ void cache_init_kernel(int BG, int w, int s, CacheView c) {
 // One workgroup (256 threads) per (batch, KV head): bookkeeping of the cache.
 __global__ __launch_bounds__(256) void cache_meta_kernel(int Tmax, int Hkv, int s, int w, int C,
                                                          const int32_t* __restrict__ seq_lens,
+                                                         ChunkView xv,
                                                          const float* __restrict__ scores,
                                                          const int32_t* __restrict__ rank,
                                                          const int32_t* __restrict__ thr,
@@ -48,16 +54,26 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int Tmax, int Hkv, int 
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int bg = blockIdx.x;
-    const int T = seq_len_of(seq_lens, bg / Hkv, Tmax);     // this sequence's length
+    const int b = bg / Hkv;
+    const int T = seq_len_of(seq_lens, b, Tmax);            // rows of this sequence
     const float* r = scores + long(bg) * Tmax;
     const int32_t* rk = rank + long(bg) * Tmax;
     const float qnan = __builtin_nanf("");
+    // row -> token map of a chunked prefill (identity otherwise)
+    const bool warm = xv.warm != nullptr && xv.warm[b] != 0;
+    const int off = warm ? xv.tok_off[b] : 0;
+    const int Tn = T + off;                                  // tokens of the sequence
+    auto tok = [&](int e) {
+        if (!warm || e < s) return e;
+        if (e < s + C) return int(xv.seg_tok[long(bg) * C + (e - s)]);
+        return e + off;
+    };
 
-    // ring scores
+    // ring scores: the ring's tokens are the last w rows
     for (int slot = tid; slot < w; slot += 256) {
-        const int j = T - 1 - ((T - 1 - slot) % w + w) % w;   // newest token in this slot
+        const int j = Tn - 1 - ((Tn - 1 - slot) % w + w) % w;   // newest token in this slot
         float sc = qnan;
-        if (j >= 0 && j >= s && j <= T - 3) sc = r[j];
+        if (j >= 0 && j >= s && j <= Tn - 3) sc = r[j - off];
         c.ring_score[long(bg) * w + slot] = sc;
     }
 
@@ -89,12 +105,13 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int Tmax, int Hkv, int 
                 woff += (x < wave) ? wsum[x] : 0;
                 tot += wsum[x];
             }
-            const int off = len + woff + incl - cnt;
+            const int o = len + woff + incl - cnt;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (u < cnt) {
-                    c.ret_idx[long(bg) * C + off + u] = ent[u];
-                    c.ret_score[long(bg) * C + off + u] = r[ent[u]];
+                    c.ret_idx[long(bg) * C + o + u] = tok(ent[u]);
+                    c.ret_score[long(bg) * C + o + u] = r[ent[u]];
+                    if (xv.seg_row != nullptr) xv.seg_row[long(bg) * C + o + u] = ent[u];
                 }
             }
             len += tot;
@@ -131,17 +148,17 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int Tmax, int Hkv, int 
     }
     if (tid == 0) {
         c.count[bg] = len;
-        c.pos[bg] = T;
-        c.next_unscored[bg] = max(T - 2, s);
+        c.pos[bg] = Tn;
+        c.next_unscored[bg] = max(Tn - 2, s);
         c.flags[bg] = 0;
         c.weak[bg] = wx;
-        // decision for the token T-w that leaves at the first decode step (its
-        // score is final: its right neighbours T-w+1, T-w+2 exist)
+        // decision for the token Tn-w that leaves at the first decode step (its
+        // score is final: its right neighbours Tn-w+1, Tn-w+2 exist)
         int nx = -1;
         float rl = 0.0f;
-        const int jl = T - w;
+        const int jl = Tn - w;
         if (jl >= s) {
-            rl = r[jl];
+            rl = r[jl - off];
             if (rl > 0.5f && C > 0) {
                 if (len < C) nx = len;
                 else if (wx >= 0 && rl > c.ret_score[long(bg) * C + wx]) nx = wx;
@@ -158,6 +175,7 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int Tmax, int Hkv, int 
 __global__ __launch_bounds__(256) void cache_copy_kernel(int Tmax, int Hkv, int D, int s, int w,
                                                          int C, int S, int slots_per_block,
                                                          const int32_t* __restrict__ seq_lens,
+                                                         ChunkView xv,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          CacheView c) {
@@ -166,22 +184,27 @@ __global__ __launch_bounds__(256) void cache_copy_kernel(int Tmax, int Hkv, int 
     const int sb = blockIdx.x % nsb;
     const int b = bg / Hkv;
     const int g = bg % Hkv;
-    const int T = seq_len_of(seq_lens, b, Tmax);            // this sequence's length
+    const int T = seq_len_of(seq_lens, b, Tmax);            // rows of this sequence
+    const bool warm = xv.warm != nullptr && xv.warm[b] != 0;
+    const int off = warm ? xv.tok_off[b] : 0;
+    const int Tn = T + off;                                  // tokens of the sequence
     const int chunks = D / 8;
     const int cnt = c.count[bg];
     for (int x = threadIdx.x; x < slots_per_block * chunks; x += blockDim.x) {
         const int slot = sb * slots_per_block + x / chunks;
         const int ch = x % chunks;
         if (slot >= S) continue;
-        int j = -1;
+        int j = -1;                                      // source row
         if (slot < s) {
             if (slot < T) j = slot;
         } else if (slot < s + C) {
-            if (slot - s < cnt) j = c.ret_idx[long(bg) * C + (slot - s)];
+            if (slot - s < cnt)
+                j = xv.seg_row != nullptr ? xv.seg_row[long(bg) * C + (slot - s)]
+                                          : c.ret_idx[long(bg) * C + (slot - s)];
         } else {
             const int rs = slot - s - C;
-            const int jj = T - 1 - ((T - 1 - rs) % w + w) % w;
-            if (jj >= 0) j = jj;
+            const int jj = Tn - 1 - ((Tn - 1 - rs) % w + w) % w;   // token
+            if (jj >= 0) j = jj - off;
         }
         if (j < 0) continue;
         const long src = ((long(b) * Tmax + j) * Hkv + g) * D + ch * 8;
@@ -204,18 +227,19 @@ hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_
 }
 
 hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_lens,
-                              const uint16_t* k, const uint16_t* v, const float* scores,
-                              const int32_t* rank, const int32_t* thr, const CacheView& cache,
-                              hipStream_t st) {
+                              const ChunkView* chunk, const uint16_t* k, const uint16_t* v,
+                              const float* scores, const int32_t* rank, const int32_t* thr,
+                              const CacheView& cache, hipStream_t st) {
     const int BG = sh.B * sh.Hkv;
+    const ChunkView x = chunk ? *chunk : ChunkView{};
     hipLaunchKernelGGL(cache_meta_kernel, dim3(BG), dim3(256), 0, st, int(T), sh.Hkv, sh.s, sh.w,
-                       sh.C, seq_lens, scores, rank, thr, cache);
+                       sh.C, seq_lens, x, scores, rank, thr, cache);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int spb = 32;                                  // slots per workgroup
     const int nsb = (sh.S + spb - 1) / spb;
     hipLaunchKernelGGL(cache_copy_kernel, dim3(unsigned(long(BG) * nsb)), dim3(256), 0, st,
-                       int(T), sh.Hkv, sh.D, sh.s, sh.w, sh.C, sh.S, spb, seq_lens, k, v,
+                       int(T), sh.Hkv, sh.D, sh.s, sh.w, sh.C, sh.S, spb, seq_lens, x, k, v,
                        cache);
     return hipGetLastError();
 }

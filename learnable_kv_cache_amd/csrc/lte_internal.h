@@ -93,6 +93,19 @@ struct CacheView {
     int32_t* arrive;       // [B][Hkv] decode split arrivals, 0 between calls
 };
 
+// Per-call data of a chunked prefill (device arrays in the workspace): the
+// extended sequence of each batch entry and its row -> token map.
+struct ChunkView {
+    int32_t* ext_len;      // [B]  rows of the extended sequence
+    int32_t* q_lo;         // [B]  first chunk row
+    int32_t* tok_off;      // [B]  token = row + tok_off past the segment rows
+    int32_t* warm;         // [B]  1: sink/segment/ring layout, 0: the whole history
+    int32_t* score_lo;     // [B][Hkv] first row whose score is computed
+    int32_t* seg_tok;      // [B][Hkv][C] tokens of the sorted segment rows
+    int32_t* seg_slot;     // [B][Hkv][C] their cache slots - s, -1 past count
+    int32_t* seg_row;      // [B][Hkv][C] rows of the new segment entries
+};
+
 inline CacheView cache_view(const Shape& sh, void* base) {
     lte_cache_layout L = cache_layout(sh);
     char* p = static_cast<char*>(base);
@@ -179,20 +192,30 @@ inline WsLayout ws_layout(const Shape& sh, int64_t T) {
 hipError_t launch_pack_w1(const Shape& sh, const float* w1, uint16_t* w1p, hipStream_t st);
 // Prefill launchers: T is the row count of every [B][T] tensor; seq_lens (device,
 // [B], or null for T everywhere) gives each sequence's length.
+// score_lo (device, [B][Hkv], or null): rows below it are left as they are.
 hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
-                                const uint16_t* k, const uint16_t* v, const uint16_t* w1p,
-                                const lte_cnn& cnn, float* scores, hipStream_t st);
+                                const int32_t* score_lo, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* w1p, const lte_cnn& cnn, float* scores,
+                                hipStream_t st);
 hipError_t launch_select(const Shape& sh, int64_t T, const int32_t* seq_lens, const float* scores,
                          int32_t* rank, int32_t* thr, int32_t* ncand, uint32_t* scratch,
                          hipStream_t st);
+// q_lo (device, [B], or null): only rows >= q_lo[b] are queries; q and out are
+// then [B][q_rows][Hq][D] with row i at i - q_lo[b].
 hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
-                                 const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                 const int32_t* rank, const int32_t* thr, uint16_t* out,
-                                 hipStream_t st);
+                                 const int32_t* q_lo, int q_rows, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, const int32_t* rank,
+                                 const int32_t* thr, uint16_t* out, hipStream_t st);
+// chunk (or null): the rows are a chunked prefill's extended sequence.
 hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_lens,
-                              const uint16_t* k, const uint16_t* v, const float* scores,
-                              const int32_t* rank, const int32_t* thr, const CacheView& cache,
-                              hipStream_t st);
+                              const ChunkView* chunk, const uint16_t* k, const uint16_t* v,
+                              const float* scores, const int32_t* rank, const int32_t* thr,
+                              const CacheView& cache, hipStream_t st);
+// Extended sequence of a chunked prefill: layout data, known scores (into
+// ext_scores [B][Hkv][Emax]) and K/V rows (ek, ev [B][Emax][Hkv][D]).
+hipError_t launch_chunk_gather(const Shape& sh, int n, int Emax, const uint16_t* k,
+                               const uint16_t* v, const CacheView& cache, const ChunkView& x,
+                               float* ext_scores, uint16_t* ek, uint16_t* ev, hipStream_t st);
 hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_t st);
 hipError_t launch_score_evict(const Shape& sh, const lte_cnn& cnn, const uint16_t* k_t,
                               const uint16_t* v_t, const CacheView& cache, hipStream_t st);

@@ -11,7 +11,8 @@
 // Grid: one workgroup per 124 consecutive tokens of one (batch, KV head).
 // Tokens outside [0, T_b) read as zero (first layer's padding) and their hidden
 // activations are zero (second layer's padding); T_b is the sequence's length
-// (seq_lens[b], or T for every sequence).
+// (seq_lens[b], or T for every sequence).  With score_lo (per (b, g)), rows
+// below it are not written: they hold scores already known.
 #include "score_core.h"
 
 namespace lte {
@@ -39,7 +40,8 @@ __global__ void pack_w1_kernel(int Hkv, int D, const float* __restrict__ w1,
 template <int D>
 __global__ __launch_bounds__(256) void score_prefill_kernel(
     int T, int Hkv, int ntile, const int32_t* __restrict__ seq_lens,
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ score_lo, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v,
     const bf16x8* __restrict__ w1p, const float* __restrict__ b1, const float* __restrict__ w2,
     const float* __restrict__ b2, float* __restrict__ scores) {
     __shared__ __align__(16) unsigned char buf[ScoreSmem<D>::kBytes];
@@ -54,6 +56,8 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     const int t0 = tile * kScoreTile;
     const int Tb = seq_len_of(seq_lens, b, T);
     if (t0 >= Tb) return;                                    // the whole tile is padding
+    const int lo = score_lo ? score_lo[bg] : 0;              // rows below keep their scores
+    if (t0 + kScoreTile <= lo) return;
 
     bf16x8* wl = reinterpret_cast<bf16x8*>(buf);
     const bf16x8* wsrc = w1p + long(g) * NW;
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
             return true;
         },
         [&](int x) { return x < 0 || x >= Tb; },
-        [&](int t, float r) { out[t] = r; });
+        [&](int t, float r) { if (t >= lo) out[t] = r; });
 }
 
 }  // namespace
@@ -88,17 +92,18 @@ hipError_t launch_pack_w1(const Shape& sh, const float* w1, uint16_t* w1p, hipSt
 }
 
 hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
-                                const uint16_t* k, const uint16_t* v, const uint16_t* w1p,
-                                const lte_cnn& cnn, float* scores, hipStream_t st) {
+                                const int32_t* score_lo, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* w1p, const lte_cnn& cnn, float* scores,
+                                hipStream_t st) {
     const int ntile = int((T + kScoreTile - 1) / kScoreTile);
     dim3 grid(unsigned(long(sh.B) * sh.Hkv * ntile));
     const bf16x8* wp = reinterpret_cast<const bf16x8*>(w1p);
     if (sh.D == 128) {
         hipLaunchKernelGGL(score_prefill_kernel<128>, grid, dim3(256), 0, st, int(T), sh.Hkv,
-                           ntile, seq_lens, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+                           ntile, seq_lens, score_lo, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
     } else {
         hipLaunchKernelGGL(score_prefill_kernel<64>, grid, dim3(256), 0, st, int(T), sh.Hkv,
-                           ntile, seq_lens, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+                           ntile, seq_lens, score_lo, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
     }
     return hipGetLastError();
 }

@@ -67,6 +67,8 @@ SIGNATURES = {
     "lte_prefill": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _CNNP, _P, _P, _P, _SZ, _P, _P]),
     "lte_prefill_varlen": (ctypes.c_int,
                            [_CFG, _I64, _P, _P, _P, _P, _CNNP, _P, _P, _P, _SZ, _P, _P]),
+    "lte_chunk_workspace_bytes": (_SZ, [_CFG, _I64]),
+    "lte_prefill_chunk": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _CNNP, _P, _P, _SZ, _P, _P]),
     "lte_prefill_score": (ctypes.c_int, [_CFG, _I64, _P, _P, _CNNP, _P, _SZ, _P]),
     "lte_prefill_select": (ctypes.c_int, [_CFG, _I64, _P, _P, _SZ, _P]),
     "lte_prefill_attend": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _P, _SZ, _P, _P]),
@@ -210,6 +212,32 @@ class Layer:
                 ctypes.byref(self._c), int(T), _ptr(seq_lens), _ptr(q), _ptr(k), _ptr(v), cnn_p,
                 _ptr(score_override), _ptr(cache), _ptr(workspace), int(workspace.numel()),
                 _ptr(out), _stream()), "lte_prefill_varlen")
+        return out
+
+    def chunk_workspace_bytes(self, n: int) -> int:
+        return int(lib().lte_chunk_workspace_bytes(ctypes.byref(self._c), int(n)))
+
+    def alloc_chunk_workspace(self, n: int, device="cuda") -> torch.Tensor:
+        nbytes = self.chunk_workspace_bytes(n)
+        if nbytes == 0:
+            raise ValueError(f"chunk of {n} tokens not supported for this layer")
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def prefill_chunk(self, q, k, v, cnn: CNN, cache, workspace=None, out=None):
+        """Appends n tokens per sequence to the cache and returns their outputs."""
+        c = self.cfg
+        n = q.shape[1]
+        _need(q, torch.bfloat16, (c.batch, n, c.q_heads, c.head_dim), "q")
+        _need(k, torch.bfloat16, (c.batch, n, c.kv_heads, c.head_dim), "k")
+        _need(v, torch.bfloat16, (c.batch, n, c.kv_heads, c.head_dim), "v")
+        if workspace is None:
+            workspace = self.alloc_chunk_workspace(n, q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        _check(lib().lte_prefill_chunk(
+            ctypes.byref(self._c), int(n), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cnn.c),
+            _ptr(cache), _ptr(workspace), int(workspace.numel()), _ptr(out), _stream()),
+            "lte_prefill_chunk")
         return out
 
     def prefill_score(self, k, v, cnn: CNN, workspace):

@@ -88,6 +88,19 @@ def test_calls_fail_before_launch_on_bad_arguments():
     assert VL(cfg, 40000, fake, fake, fake, fake, None, fake, None, fake, ws, fake, None) == 2
     assert VL(cfg, T, fake, fake, fake, fake, None, None, None, fake, ws, fake, None) == 1
     assert VL(cfg, T, fake, fake, fake, fake, None, fake, None, fake, ws - 1, fake, None) == 5
+    # chunked prefill: bad n, null cache, small workspace, n past the row limit
+    good_cnn = lte._CNN(0x1000, 0x1000, 0x1000, 0x1000)
+    cw = L.lte_chunk_workspace_bytes(cfg, 8)
+    assert cw > 0 and L.lte_chunk_workspace_bytes(cfg, 0) == 0
+    assert L.lte_chunk_workspace_bytes(cfg, 40000) == 0
+    CH = L.lte_prefill_chunk
+    assert CH(cfg, 0, fake, fake, fake, ctypes.byref(good_cnn), fake, fake, cw, fake, None) == 1
+    assert CH(cfg, 8, fake, fake, fake, ctypes.byref(good_cnn), None, fake, cw, fake, None) == 1
+    assert CH(cfg, 8, fake, fake, fake, None, fake, fake, cw, fake, None) == 1
+    assert CH(cfg, 8, fake, fake, fake, ctypes.byref(good_cnn), fake, fake, cw - 1, fake,
+              None) == 5
+    assert CH(cfg, 40000, fake, fake, fake, ctypes.byref(good_cnn), fake, fake, cw, fake,
+              None) == 2
     # decode: null cache, small workspace, CNN with a null member
     assert L.lte_decode_attend(cfg, fake, None, fake, 1 << 30, fake, None) == 1
     assert L.lte_decode_attend(cfg, fake, fake, fake, 16, fake, None) == 5
