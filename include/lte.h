@@ -277,6 +277,41 @@ int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* 
 int lte_cache_export(const lte_config* cfg, const void* cache, int32_t* ret_idx,
                      float* ret_score, int32_t* count, int64_t* pos, void* stream);
 
+/* ===========================================================================
+ * Linear-attention layer of the hybrid ("Sparse Linear Attention: Viewing SWA
+ * from the Perspective of Linear Attention", section "Background: Linear
+ * attention"):  S_t = S_{t-1} A_t + v_t k_t^T,  o_t = S_t q_t, with
+ * A_t = a_t I: one decay a_t = exp(log_a) in [0, 1] per head and step (1 is
+ * naive linear attention; log_a below -80 acts as -80, a reset).  No scaling
+ * or feature map of q and k.  S is D x D per (batch, head), fp32.
+ * ========================================================================= */
+typedef struct {
+    int32_t batch;      /* B                               */
+    int32_t heads;      /* H (q, k and v alike)            */
+    int32_t head_dim;   /* D in {64, 128}                  */
+} lte_linear_config;
+
+int lte_linear_check_config(const lte_linear_config* cfg);
+/* Bytes of the states of all (batch, head): B * H * D * D * 4. */
+size_t lte_linear_state_bytes(const lte_linear_config* cfg);
+
+/* The layer over T tokens (1 <= T <= 2^22).
+ *   q, k, v  bf16 [B][T][H][D];  log_a fp32 [B][T][H]
+ *   state_in  fp32 [B][H][D][D] (S[value dim][key dim]) the state before the
+ *       first token, or NULL for zero; may be the same buffer as state_out
+ *   state_out fp32 [B][H][D][D] the state after the last token
+ *   out  bf16 [B][T][H][D] */
+int lte_linear_prefill(const lte_linear_config* cfg, int64_t T,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const float* log_a, const float* state_in, float* state_out,
+                       uint16_t* out, void* stream);
+
+/* One token: q_t, k_t, v_t bf16 [B][H][D], log_a_t fp32 [B][H]; state fp32
+ * [B][H][D][D] updated in place; out_t bf16 [B][H][D]. */
+int lte_linear_decode_step(const lte_linear_config* cfg, const uint16_t* q_t,
+                           const uint16_t* k_t, const uint16_t* v_t, const float* log_a_t,
+                           float* state, uint16_t* out_t, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -330,6 +330,40 @@ int lte_prefill_chunk(const lte_config* cfg, int64_t n, const uint16_t* q, const
         launch_build_cache(sh, E, x.ext_len, &x, ek, ev, w.scores, w.rank, w.thr, c, st));
 }
 
+int lte_linear_check_config(const lte_linear_config* cfg) {
+    if (cfg == nullptr) return LTE_ERR_INVALID_ARG;
+    if (cfg->batch < 1 || cfg->heads < 1 || cfg->head_dim < 1) return LTE_ERR_INVALID_ARG;
+    if (cfg->head_dim != 64 && cfg->head_dim != 128) return LTE_ERR_UNSUPPORTED;
+    if (int64_t(cfg->batch) * cfg->heads > (int64_t(1) << 24)) return LTE_ERR_UNSUPPORTED;
+    return LTE_OK;
+}
+
+size_t lte_linear_state_bytes(const lte_linear_config* cfg) {
+    if (lte_linear_check_config(cfg) != LTE_OK) return 0;
+    return size_t(cfg->batch) * cfg->heads * cfg->head_dim * cfg->head_dim * sizeof(float);
+}
+
+int lte_linear_prefill(const lte_linear_config* cfg, int64_t T, const uint16_t* q,
+                       const uint16_t* k, const uint16_t* v, const float* log_a,
+                       const float* state_in, float* state_out, uint16_t* out, void* stream) {
+    LTE_TRY(lte_linear_check_config(cfg));
+    if (T < 1) return LTE_ERR_INVALID_ARG;
+    if (T > kMaxLinearT) return LTE_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !log_a || !state_out || !out) return LTE_ERR_INVALID_ARG;
+    return hip_status(launch_linear_prefill(cfg->batch, cfg->heads, cfg->head_dim, T, q, k, v,
+                                            log_a, state_in, state_out, out,
+                                            hipStream_t(stream)));
+}
+
+int lte_linear_decode_step(const lte_linear_config* cfg, const uint16_t* q_t, const uint16_t* k_t,
+                           const uint16_t* v_t, const float* log_a_t, float* state,
+                           uint16_t* out_t, void* stream) {
+    LTE_TRY(lte_linear_check_config(cfg));
+    if (!q_t || !k_t || !v_t || !log_a_t || !state || !out_t) return LTE_ERR_INVALID_ARG;
+    return hip_status(launch_linear_step(cfg->batch, cfg->heads, cfg->head_dim, q_t, k_t, v_t,
+                                         log_a_t, state, out_t, hipStream_t(stream)));
+}
+
 int lte_score_evict(const lte_config* cfg, const lte_cnn* cnn, const uint16_t* k_t,
                     const uint16_t* v_t, void* cache, void* stream) {
     LTE_TRY(check_cfg(cfg));

@@ -1,0 +1,328 @@
+// Linear-attention layer of the hybrid: S_t = a_t S_{t-1} + v_t k_t^T,
+// o_t = S_t q_t, one decay a_t per head and step.
+//
+// "Sparse Linear Attention: Viewing SWA from the Perspective of Linear
+// Attention", section "Background: Linear attention": the state is decayed by
+// A_t, written with v_t k_t^T and read with q_t.  A_t = a_t I here, given as
+// log a_t; no scaling or feature map of q and k.
+//
+// Prefill, chunkwise (64 tokens per chunk, one workgroup per (batch, head),
+// the state S^T in MFMA accumulators across chunks).  With G_t the running sum
+// of log a over the chunk up to t (inclusive) and S0 the state before it:
+//   o_t   = exp(G_t) S0 q_t + sum_{j <= t in chunk} exp(G_t - G_j) (q_t.k_j) v_j
+//   S_end = exp(G_last) S0 + sum_j exp(G_last - G_j) v_j k_j^T
+// Every exponent is <= 0.  Four MFMA products per chunk (v_mfma_f32_32x32x16_bf16):
+//   P^T = K Q^T (masked and decayed, bf16, shared through LDS);
+//   O  += P V (intra-chunk);  O' = Q S0^T (inter-chunk, S0 rounded to bf16);
+//   S^T = exp(G_last) S^T + (w K)^T V  with w_j = exp(G_last - G_j).
+// Wave w owns the 32 output dims [32w, 32w+32) of O and of S^T.  An MFMA
+// accumulator holds its column in lane & 31 and rows (e/4)*8 + (lane/32)*4 +
+// e%4; read as a 16-wide k operand, element i of lane-half h is then row
+// 16c + (i<4 ? 4h + i : 8 + 4h + i-4) of step c, and every other operand is
+// read in that same k order.
+#include "lte_internal.h"
+
+namespace lte {
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;
+constexpr float kLogAMin = -80.0f;     // a < 1.8e-35 acts as a reset
+
+// 16-byte chunk swizzles.  Row-strided b128 reads of 16 consecutive rows (Q,
+// K) and transposing b64 reads of 4 consecutive rows x 64 bytes (V, w K)
+// each spread over all banks.
+template <int D>
+__device__ __forceinline__ int rswz(int r) {
+    if constexpr (D == 128) return (((r & 1) * 10) | ((r & 2) << 1)) ^ ((r >> 2) & 3);
+    else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
+template <int D>
+__device__ __forceinline__ int tswz(int r) {
+    if constexpr (D == 128) return (r & 3) << 2;
+    else return ((r >> 1) & 1) << 2;
+}
+// P tile [64 t][64 j]: 8 chunks per 128-byte row
+__device__ __forceinline__ int pswz(int t) { return (t >> 1) & 7; }
+
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void linear_prefill_kernel(
+    int T, int H, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ log_a,
+    const float* __restrict__ state_in, float* __restrict__ state_out,
+    uint16_t* __restrict__ out) {
+    constexpr int NW = D / 32;              // waves; wave w owns dims [32w, 32w+32)
+    constexpr int NT = 64 * NW;
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int KK = D / 16;              // k-steps over D
+    constexpr int DT = D / 32;              // 32-row tiles over D
+    __shared__ __align__(16) u32x4 Qs[kChunk * CPR];
+    __shared__ __align__(16) u32x4 Ks[kChunk * CPR];
+    __shared__ __align__(16) u32x4 Vs[kChunk * CPR];
+    __shared__ __align__(16) u32x4 Ws[kChunk * CPR];     // w_j K[j]
+    __shared__ __align__(16) u32x4 Ps[kChunk * 8];       // P[t][j] bf16
+    __shared__ float Gs[kChunk];                          // G_t
+    __shared__ float Es[kChunk];                          // exp(G_t)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const int h = bh % H;
+    const long rs = long(H) * D;                          // row stride of q, k, v, out
+
+    // ---- state S^T: tile kt holds S^T[kt*32 + row(e)][32*wave + lane&31] ----------
+    f32x16 st[DT];
+    const float* sin = state_in ? state_in + long(bh) * D * D : nullptr;
+    const int dcol = 32 * wave + (lane & 31);
+#pragma unroll
+    for (int kt = 0; kt < DT; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int kr = kt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+            st[kt][e] = sin ? sin[long(dcol) * D + kr] : 0.0f;     // S[d][k]
+        }
+    }
+    // per-lane pieces of the transposing reads (see the attention kernel): lane
+    // (16-group G, index i) reads rows 4*(G>>1) + (i>>2) (+16c + 8r) at dims
+    // (G&1)*16 + 4*(i&3) of a 32-wide tile
+    uint32_t trd[DT];
+    {
+        const int grp = lane >> 4;
+        const int i = lane & 15;
+        const int key0 = 4 * (grp >> 1) + (i >> 2);
+        const int c_lo = 2 * (grp & 1) + ((i & 3) >> 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            trd[dt] = uint32_t(key0 * CPR * 16 + ((4 * dt + c_lo) ^ tswz<D>(key0)) * 16 + 8 * (i & 1));
+    }
+    auto tr_operand = [&](const u32x4* tile, int dt, int c) {
+        const char* base = reinterpret_cast<const char*>(tile);
+        bf16x8 a;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(base + trd[dt] +
+                                                           (c * 16 + 8 * r) * CPR * 16));
+            const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
+            a[4 * r + 0] = b4[0];
+            a[4 * r + 1] = b4[1];
+            a[4 * r + 2] = b4[2];
+            a[4 * r + 3] = b4[3];
+        }
+        return a;
+    };
+
+    const int nchunk = (T + kChunk - 1) / kChunk;
+    for (int ch = 0; ch < nchunk; ++ch) {
+        const int t0 = ch * kChunk;
+        const int nrow = min(kChunk, T - t0);
+        // ---- load the chunk: q, k, v rows (zero past T), log a ----------------------
+        for (int x = tid; x < kChunk * CPR; x += NT) {
+            const int r = x / CPR;
+            const int c = x % CPR;
+            u32x4 qv = {0u, 0u, 0u, 0u}, kv = qv, vv = qv;
+            if (r < nrow) {
+                const long src = (long(b) * T + t0 + r) * rs + long(h) * D + c * 8;
+                qv = *reinterpret_cast<const u32x4*>(q + src);
+                kv = *reinterpret_cast<const u32x4*>(k + src);
+                vv = *reinterpret_cast<const u32x4*>(v + src);
+            }
+            Qs[r * CPR + (c ^ rswz<D>(r))] = qv;
+            Ks[r * CPR + (c ^ rswz<D>(r))] = kv;
+            Vs[r * CPR + (c ^ tswz<D>(r))] = vv;
+        }
+        if (wave == 0) {
+            float g = (lane < nrow) ? fmaxf(log_a[(long(b) * T + t0 + lane) * H + h], kLogAMin)
+                                    : 0.0f;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float y = __shfl_up(g, d, 64);
+                if (lane >= d) g += y;
+            }
+            Gs[lane] = g;
+            Es[lane] = __expf(g);
+        }
+        __syncthreads();
+        // ---- w K: row j scaled by exp(G_last - G_j) ------------------------------------
+        const float g_last = Gs[kChunk - 1];
+        for (int x = tid; x < kChunk * CPR; x += NT) {
+            const int r = x / CPR;
+            const float wj = __expf(g_last - Gs[r]);
+            const int pc = x % CPR;                       // physical chunk of Ks row r
+            const int c = pc ^ rswz<D>(r);                // its logical chunk
+            const bf16x8 kv = __builtin_bit_cast(bf16x8, Ks[r * CPR + pc]);
+            bf16x8 wv;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) wv[u] = (__bf16)(float(kv[u]) * wj);
+            Ws[r * CPR + (c ^ tswz<D>(r))] = __builtin_bit_cast(u32x4, wv);
+        }
+        // ---- P^T = K Q^T for the tiles (jt, tt) of this wave; mask, decay, to LDS ----
+        for (int tile = wave; tile < 4; tile += NW) {
+            const int jt = tile & 1;
+            const int tt = tile >> 1;
+            f32x16 sacc = f32x16{};
+            const int jr = jt * 32 + (lane & 31);
+            const int tr = tt * 32 + (lane & 31);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, Ks[jr * CPR + ((2 * kk + half) ^ rswz<D>(jr))]);
+                const bf16x8 bq = __builtin_bit_cast(
+                    bf16x8, Qs[tr * CPR + ((2 * kk + half) ^ rswz<D>(tr))]);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, sacc, 0, 0, 0);
+            }
+            const float gt = Gs[tr];
+            bf16x8 pf[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = jt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                const float p = (j <= tr) ? sacc[e] * __expf(gt - Gs[j]) : 0.0f;
+                pf[e >> 3][e & 7] = (__bf16)p;
+            }
+            // P row tr, k-step c = 2jt + s, lane-half h: chunk 2c + h
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int pc = (2 * (2 * jt + s2) + half) ^ pswz(tr);
+                Ps[tr * 8 + pc] = __builtin_bit_cast(u32x4, pf[s2]);
+            }
+        }
+        __syncthreads();
+
+        // ---- V operands of this wave's dims, k-steps c = 0..3 (P V and the update) ----
+        bf16x8 vop[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vop[c] = tr_operand(Vs, wave, c);
+        // ---- O = P V + exp(G_t) Q S0^T for both row tiles ------------------------------
+        bf16x8 sop[KK];                                   // S0^T as bf16 k operands
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sop[kk][i] = (__bf16)st[kk >> 1][(kk & 1) * 8 + i];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int tr = tt * 32 + (lane & 31);
+            f32x16 oi = f32x16{}, ox = f32x16{};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bf16x8 pa = __builtin_bit_cast(bf16x8, Ps[tr * 8 + ((2 * c + half) ^ pswz(tr))]);
+                oi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vop[c], oi, 0, 0, 0);
+            }
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                // q[tr][16kk + 4h .. +4] and q[tr][16kk + 8 + 4h .. +4]: halves of chunks
+                const uint16_t* row = reinterpret_cast<const uint16_t*>(Qs + tr * CPR);
+                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(
+                    row + ((2 * kk) ^ rswz<D>(tr)) * 8 + 4 * half);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(
+                    row + ((2 * kk + 1) ^ rswz<D>(tr)) * 8 + 4 * half);
+                const bf16x8 qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                ox = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sop[kk], ox, 0, 0, 0);
+            }
+            // element e: row t = tt*32 + (e/4)*8 + h*4 + e%4, dim 32*wave + lane&31
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = tt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                if (t < nrow) {
+                    const float o = oi[e] + Es[t] * ox[e];
+                    out[(long(b) * T + t0 + t) * rs + long(h) * D + dcol] =
+                        __builtin_bit_cast(uint16_t, (__bf16)o);
+                }
+            }
+        }
+        // ---- S^T = exp(G_last) S^T + (w K)^T V ----------------------------------------
+        const float decay = __expf(g_last);
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt) {
+            st[kt] *= decay;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bf16x8 wa = tr_operand(Ws, kt, c);
+                st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, vop[c], st[kt], 0, 0, 0);
+            }
+        }
+        __syncthreads();                                  // the chunk's tiles are free
+    }
+    float* so = state_out + long(bh) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int kr = kt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+            so[long(dcol) * D + kr] = st[kt][e];
+        }
+}
+
+// One step: S <- a S + v k^T, o = S q.  One workgroup of 256 threads per
+// (batch, head); thread x owns D*D/256 consecutive elements of one row of S.
+template <int D>
+__global__ __launch_bounds__(256) void linear_step_kernel(int H, const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const float* __restrict__ log_a,
+                                                          float* __restrict__ state,
+                                                          uint16_t* __restrict__ out) {
+    constexpr int PER = D * D / 256;                      // elements per thread
+    constexpr int TPR = D / PER;                          // threads per row
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int d = tid / TPR;                              // row of S (value dim)
+    const int k0 = (tid % TPR) * PER;                     // first key dim
+    const float a = __expf(fmaxf(log_a[bh], kLogAMin));
+    const float vd = float(__builtin_bit_cast(__bf16, v[long(bh) * D + d]));
+    float* srow = state + long(bh) * D * D + long(d) * D + k0;
+    const uint16_t* kp = k + long(bh) * D + k0;
+    const uint16_t* qp = q + long(bh) * D + k0;
+    float acc = 0.0f;
+#pragma unroll
+    for (int x = 0; x < PER; x += 4) {
+        float4 s4 = *reinterpret_cast<const float4*>(srow + x);
+        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(kp + x);
+        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(qp + x);
+        s4.x = fmaf(a, s4.x, vd * float(k4[0]));
+        s4.y = fmaf(a, s4.y, vd * float(k4[1]));
+        s4.z = fmaf(a, s4.z, vd * float(k4[2]));
+        s4.w = fmaf(a, s4.w, vd * float(k4[3]));
+        acc = fmaf(s4.x, float(q4[0]), acc);
+        acc = fmaf(s4.y, float(q4[1]), acc);
+        acc = fmaf(s4.z, float(q4[2]), acc);
+        acc = fmaf(s4.w, float(q4[3]), acc);
+        *reinterpret_cast<float4*>(srow + x) = s4;
+    }
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (tid % TPR == 0) out[long(bh) * D + d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+}
+
+}  // namespace
+
+hipError_t launch_linear_prefill(int B, int H, int D, int64_t T, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, const float* log_a,
+                                 const float* state_in, float* state_out, uint16_t* out,
+                                 hipStream_t st) {
+    dim3 grid(unsigned(B * H));
+    if (D == 128)
+        hipLaunchKernelGGL(linear_prefill_kernel<128>, grid, dim3(256), 0, st, int(T), H, q, k, v,
+                           log_a, state_in, state_out, out);
+    else
+        hipLaunchKernelGGL(linear_prefill_kernel<64>, grid, dim3(128), 0, st, int(T), H, q, k, v,
+                           log_a, state_in, state_out, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_step(int B, int H, int D, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const float* log_a, float* state, uint16_t* out,
+                              hipStream_t st) {
+    dim3 grid(unsigned(B * H));
+    if (D == 128)
+        hipLaunchKernelGGL(linear_step_kernel<128>, grid, dim3(256), 0, st, H, q, k, v, log_a,
+                           state, out);
+    else
+        hipLaunchKernelGGL(linear_step_kernel<64>, grid, dim3(256), 0, st, H, q, k, v, log_a,
+                           state, out);
+    return hipGetLastError();
+}
+
+}  // namespace lte

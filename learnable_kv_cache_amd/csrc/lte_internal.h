@@ -25,6 +25,7 @@ constexpr int kHidden = 32;         // scoring-CNN width
 constexpr int kMaxSink = 256;
 constexpr int kMaxCapacity = 4096;
 constexpr int64_t kMaxT = 32768;     // the selection sort keeps <= 32 keys per thread
+constexpr int64_t kMaxLinearT = int64_t(1) << 22;   // linear layer: tokens per call
 constexpr int32_t kNotCand = 0x7fffffff;   // rank of a non-candidate
 constexpr int32_t kAllPass = 0x7ffffffe;   // thr when every candidate is kept
 
@@ -211,6 +212,17 @@ hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_len
                               const ChunkView* chunk, const uint16_t* k, const uint16_t* v,
                               const float* scores, const int32_t* rank, const int32_t* thr,
                               const CacheView& cache, hipStream_t st);
+// Linear-attention layer: q, k, v [B][T][H][D] bf16, log_a [B][T][H] fp32,
+// states [B][H][D][D] fp32 (S[dv][dk]); state_in may be null (zero state) and
+// may equal state_out.
+hipError_t launch_linear_prefill(int B, int H, int D, int64_t T, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, const float* log_a,
+                                 const float* state_in, float* state_out, uint16_t* out,
+                                 hipStream_t st);
+// One step: q, k, v [B][H][D], log_a [B][H], state in place, out [B][H][D].
+hipError_t launch_linear_step(int B, int H, int D, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const float* log_a, float* state, uint16_t* out,
+                              hipStream_t st);
 // Extended sequence of a chunked prefill: layout data, known scores (into
 // ext_scores [B][Hkv][Emax]) and K/V rows (ek, ev [B][Emax][Hkv][D]).
 hipError_t launch_chunk_gather(const Shape& sh, int n, int Emax, const uint16_t* k,

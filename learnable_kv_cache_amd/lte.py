@@ -45,6 +45,10 @@ class _CacheLayout(ctypes.Structure):
                  "next_unscored", "flags", "weak", "nx_slot", "nx_score", "arrive", "total")]
 
 
+class _LinConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "heads", "head_dim")]
+
+
 class _WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("scores", "rank", "thr", "ncand", "total")]
 
@@ -55,6 +59,7 @@ _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _CFG = ctypes.POINTER(_Config)
 _CNNP = ctypes.POINTER(_CNN)
+_LCFG = ctypes.POINTER(_LinConfig)
 SIGNATURES = {
     "lte_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lte_version": (ctypes.c_int, []),
@@ -68,6 +73,10 @@ SIGNATURES = {
     "lte_prefill_varlen": (ctypes.c_int,
                            [_CFG, _I64, _P, _P, _P, _P, _CNNP, _P, _P, _P, _SZ, _P, _P]),
     "lte_chunk_workspace_bytes": (_SZ, [_CFG, _I64]),
+    "lte_linear_check_config": (ctypes.c_int, [_LCFG]),
+    "lte_linear_state_bytes": (_SZ, [_LCFG]),
+    "lte_linear_prefill": (ctypes.c_int, [_LCFG, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "lte_linear_decode_step": (ctypes.c_int, [_LCFG, _P, _P, _P, _P, _P, _P, _P]),
     "lte_prefill_chunk": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _CNNP, _P, _P, _SZ, _P, _P]),
     "lte_prefill_score": (ctypes.c_int, [_CFG, _I64, _P, _P, _CNNP, _P, _SZ, _P]),
     "lte_prefill_select": (ctypes.c_int, [_CFG, _I64, _P, _P, _SZ, _P]),
@@ -352,3 +361,49 @@ class Layer:
                "lte_cache_export")
         return {"ret_idx": ret_idx.cpu(), "ret_score": ret_score.cpu(), "count": count.cpu(),
                 "pos": pos.cpu()}
+
+
+class LinearLayer:
+    """The hybrid's linear-attention layer (S_t = a_t S_{t-1} + v_t k_t^T, o_t = S_t q_t):
+    argument marshalling for the ABI calls."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int):
+        self.batch, self.heads, self.head_dim = batch, heads, head_dim
+        self._c = _LinConfig(batch, heads, head_dim)
+        _check(lib().lte_linear_check_config(ctypes.byref(self._c)), "lte_linear_check_config")
+
+    def alloc_state(self, device="cuda") -> torch.Tensor:
+        D = self.head_dim
+        return torch.zeros((self.batch, self.heads, D, D), dtype=torch.float32, device=device)
+
+    def prefill(self, q, k, v, log_a, state_in=None, state_out=None, out=None):
+        """q, k, v [B, T, H, D] bf16, log_a [B, T, H] fp32; returns (out, state_out)."""
+        B, H, D = self.batch, self.heads, self.head_dim
+        T = q.shape[1]
+        for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+            _need(t, torch.bfloat16, (B, T, H, D), nm)
+        _need(log_a, torch.float32, (B, T, H), "log_a")
+        if state_in is not None:
+            _need(state_in, torch.float32, (B, H, D, D), "state_in")
+        if state_out is None:
+            state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        _check(lib().lte_linear_prefill(ctypes.byref(self._c), int(T), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(log_a), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                        _stream()), "lte_linear_prefill")
+        return out, state_out
+
+    def decode_step(self, q_t, k_t, v_t, log_a_t, state, out=None):
+        """q_t, k_t, v_t [B, H, D] bf16, log_a_t [B, H] fp32; state updated in place."""
+        B, H, D = self.batch, self.heads, self.head_dim
+        for t, nm in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
+            _need(t, torch.bfloat16, (B, H, D), nm)
+        _need(log_a_t, torch.float32, (B, H), "log_a_t")
+        _need(state, torch.float32, (B, H, D, D), "state")
+        if out is None:
+            out = torch.empty_like(q_t)
+        _check(lib().lte_linear_decode_step(ctypes.byref(self._c), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+                                            _ptr(log_a_t), _ptr(state), _ptr(out), _stream()),
+               "lte_linear_decode_step")
+        return out

@@ -163,3 +163,18 @@ def random_case(seed: int, B: int, T: int, Hq: int, Hkv: int, D: int, cnn_std: f
     q, k, v = make_qkv(B, T, Hq, Hkv, D, seed)
     cnn = make_cnn(Hkv, D, seed + 100, np.full((Hkv,), b2, np.float32), std=cnn_std)
     return q, k, v, cnn
+
+
+def linear_inputs(seed: int, B: int, T: int, H: int, D: int, gate_mean: float = 4.0):
+    """Inputs of the linear-attention layer as CPU tensors: q, k [B,T,H,D] bf16 with
+    std D^-1/4 (so q.k is of order 1), v [B,T,H,D] bf16 N(0,1), and the per-step
+    decay as log a [B,T,H] fp32 with a = sigmoid(N(gate_mean, 1)) (mean about 0.98
+    for gate_mean 4: a memory of some tens of tokens)."""
+    g = _gen(seed)
+    s = float(D) ** -0.25
+    q = (torch.randn((B, T, H, D), generator=g) * s).to(torch.bfloat16)
+    k = (torch.randn((B, T, H, D), generator=g) * s).to(torch.bfloat16)
+    v = torch.randn((B, T, H, D), generator=g).to(torch.bfloat16)
+    x = torch.randn((B, T, H), generator=g) + gate_mean
+    log_a = torch.nn.functional.logsigmoid(x).to(torch.float32)
+    return q, k, v, log_a
