@@ -15,11 +15,13 @@ this host.
 Beside it, the same engine as the two comparators of the LTE paper's Figure 4
 (sink + sliding-window attention with no retained segment, and full causal
 attention as a window covering the whole sequence), timed on the same inputs,
-and a chunked prefill of the next 512 tokens onto the prompt's cache.
+a chunked prefill of the next 512 tokens onto the prompt's cache, and the
+hybrid's linear-attention layer (B32, 4096 tokens, 16 heads of 128): chunked
+prefill and decode steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
                        [--no-cpu-baseline] [--no-decode] [--no-comparators]
-                       [--no-chunk] [--copy-calibration MIB]
+                       [--no-chunk] [--no-linear] [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -54,6 +56,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-linear", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="sequences the oracle runs for the CPU baseline (0: one per core)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -271,6 +274,63 @@ def comparators(inp, wl, T, dev, ndec=64):
     return res
 
 
+def linear_layer(dev, B=32, T=4096, H=16, D=128, ndec=64):
+    """The hybrid's linear-attention layer on the same batch and prompt: chunked prefill
+    (timed by events) and decode steps on the state (replayed from a graph).  Algorithmic
+    flops of the prefill per head and 64-token chunk: the causal half of q.k and of p.v
+    (L(L+1)/2 D multiply-adds each), q S (L D^2) and the state update (L D^2)."""
+    import torch
+    from learnable_kv_cache_amd import lte, synth
+    q, k, v, log_a = (x.to(dev) for x in synth.linear_inputs(11, B, T + ndec, H, D))
+    qp, kp, vp, ap = (x[:, :T].contiguous() for x in (q, k, v, log_a))
+    layer = lte.LinearLayer(B, H, D)
+    state = layer.alloc_state(dev)
+    out = torch.empty_like(qp)
+    layer.prefill(qp, kp, vp, ap, state_out=state, out=out)
+    times = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.prefill(qp, kp, vp, ap, state_out=state, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times[1:]))
+    L = 64
+    nch = T / L
+    flops = 2.0 * B * H * nch * (2 * (L * (L + 1) / 2) * D + 2 * L * D * D)
+    dq, dk, dv, da = ([x[:, T + t].contiguous() for t in range(ndec)] for x in (q, k, v, log_a))
+    dout = torch.empty_like(dq[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.decode_step(dq[0], dk[0], dv[0], da[0], state, dout)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(ndec):
+            layer.decode_step(dq[t], dk[t], dv[t], da[t], state, dout)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / ndec
+    step_bytes = 2.0 * B * H * D * D * 4 + 4 * B * H * D * 2 + B * H * 4
+    return {"shape": {"B": B, "T": T, "H": H, "D": D},
+            "prefill_ms": ms, "prefill_tokens_per_s": B * T / (ms * 1e-3),
+            "prefill_roofline": {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
+                                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                                 "frac": flops / (ms * 1e-3) / PEAK_BF16_FLOPS},
+            "decode_us_per_step": us,
+            "decode_roofline": {"bound": "hbm", "achieved": step_bytes / (us * 1e-6) / 1e9,
+                                "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                                "frac": step_bytes / (us * 1e-6) / PEAK_HBM_BPS,
+                                "bytes_per_step": step_bytes}}
+
+
 # ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
@@ -478,6 +538,8 @@ def main():
         result["chunk"] = {"n": n, "onto_position": T, "ms": ch_ms,
                            "tokens_per_s": B * n / (ch_ms * 1e-3)}
         del cws, cout
+    if not args.no_linear:
+        result["linear"] = linear_layer(dev)
     if not args.no_comparators and not args.no_decode:
         cmp = comparators(inp, wl, T, dev, ndec=min(64, ndec))
         cmp["lte"] = {"window": wl.window, "capacity": wl.capacity, "prefill_attend_ms": att_ms,

@@ -15,7 +15,10 @@
 //   P^T = K Q^T (masked and decayed, bf16, shared through LDS);
 //   O  += P V (intra-chunk);  O' = Q S0^T (inter-chunk, S0 rounded to bf16);
 //   S^T = exp(G_last) S^T + (w K)^T V  with w_j = exp(G_last - G_j).
-// Wave w owns the 32 output dims [32w, 32w+32) of O and of S^T.  An MFMA
+// 2 D/32 waves, two per SIMD: wave w takes dims [32 dw, 32 dw + 32), dw = w/2,
+// of the output rows [32 x, 32 x + 32), x = w%2, and the S^T tiles kt of its
+// dims with kt in [x D/64, (x+1) D/64); the state is shared as bf16 through
+// LDS for the inter-chunk product.  An MFMA
 // accumulator holds its column in lane & 31 and rows (e/4)*8 + (lane/32)*4 +
 // e%4; read as a 16-wide k operand, element i of lane-half h is then row
 // 16c + (i<4 ? 4h + i : 8 + 4h + i-4) of step c, and every other operand is
@@ -47,21 +50,23 @@ __device__ __forceinline__ int tswz(int r) {
 __device__ __forceinline__ int pswz(int t) { return (t >> 1) & 7; }
 
 template <int D>
-__global__ __launch_bounds__(64 * (D / 32)) void linear_prefill_kernel(
+__global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     int T, int H, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ log_a,
     const float* __restrict__ state_in, float* __restrict__ state_out,
     uint16_t* __restrict__ out) {
-    constexpr int NW = D / 32;              // waves; wave w owns dims [32w, 32w+32)
+    constexpr int DT = D / 32;              // 32-row tiles over D
+    constexpr int NW = 2 * DT;              // waves
     constexpr int NT = 64 * NW;
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int KK = D / 16;              // k-steps over D
-    constexpr int DT = D / 32;              // 32-row tiles over D
+    constexpr int KTW = DT / 2;             // state tiles per wave
     __shared__ __align__(16) u32x4 Qs[kChunk * CPR];
     __shared__ __align__(16) u32x4 Ks[kChunk * CPR];
     __shared__ __align__(16) u32x4 Vs[kChunk * CPR];
     __shared__ __align__(16) u32x4 Ws[kChunk * CPR];     // w_j K[j]
     __shared__ __align__(16) u32x4 Ps[kChunk * 8];       // P[t][j] bf16
+    __shared__ __align__(16) u32x4 Sb[KK * 2 * D];       // S^T as bf16 k operands
     __shared__ float Gs[kChunk];                          // G_t
     __shared__ float Es[kChunk];                          // exp(G_t)
     const int tid = threadIdx.x;
@@ -73,18 +78,35 @@ __global__ __launch_bounds__(64 * (D / 32)) void linear_prefill_kernel(
     const int h = bh % H;
     const long rs = long(H) * D;                          // row stride of q, k, v, out
 
-    // ---- state S^T: tile kt holds S^T[kt*32 + row(e)][32*wave + lane&31] ----------
-    f32x16 st[DT];
+    const int dw = wave >> 1;                             // dim tile
+    const int xw = wave & 1;                              // row tile; half of the state tiles
+    // ---- state S^T: tile i holds S^T[(xw KTW + i)*32 + row(e)][32 dw + lane&31] ------
+    f32x16 st[KTW];
     const float* sin = state_in ? state_in + long(bh) * D * D : nullptr;
-    const int dcol = 32 * wave + (lane & 31);
+    const int dcol = 32 * dw + (lane & 31);
 #pragma unroll
-    for (int kt = 0; kt < DT; ++kt) {
+    for (int i = 0; i < KTW; ++i) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int kr = kt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-            st[kt][e] = sin ? sin[long(dcol) * D + kr] : 0.0f;     // S[d][k]
+            const int kr = (xw * KTW + i) * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+            st[i][e] = sin ? sin[long(dcol) * D + kr] : 0.0f;      // S[d][k]
         }
     }
+    // its bf16 copy for the other waves: k-step kk, lane-half h of column d is
+    // 16-byte piece (2 kk + h) * D + d
+    auto share_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < KTW; ++i) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int kk = 2 * (xw * KTW + i) + s2;
+                bf16x8 sv;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) sv[u] = (__bf16)st[i][s2 * 8 + u];
+                Sb[(2 * kk + half) * D + dcol] = __builtin_bit_cast(u32x4, sv);
+            }
+        }
+    };
     // per-lane pieces of the transposing reads (see the attention kernel): lane
     // (16-group G, index i) reads rows 4*(G>>1) + (i>>2) (+16c + 8r) at dims
     // (G&1)*16 + 4*(i&3) of a 32-wide tile
@@ -115,28 +137,41 @@ __global__ __launch_bounds__(64 * (D / 32)) void linear_prefill_kernel(
         return a;
     };
 
-    const int nchunk = (T + kChunk - 1) / kChunk;
-    for (int ch = 0; ch < nchunk; ++ch) {
-        const int t0 = ch * kChunk;
-        const int nrow = min(kChunk, T - t0);
-        // ---- load the chunk: q, k, v rows (zero past T), log a ----------------------
-        for (int x = tid; x < kChunk * CPR; x += NT) {
+    // ---- chunk loads: fetched into registers one chunk ahead, stored to LDS at the
+    //      chunk boundary (q, k, v rows zero past T; log a clamped, zero past T) ------
+    constexpr int LPT = kChunk * CPR / NT;               // 16-byte pieces per thread
+    u32x4 pq[LPT], pk[LPT], pv[LPT];
+    float pg = 0.0f;
+    auto fetch = [&](int c0) {
+        const int nr = min(kChunk, T - c0);
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int x = tid + u * NT;
             const int r = x / CPR;
             const int c = x % CPR;
-            u32x4 qv = {0u, 0u, 0u, 0u}, kv = qv, vv = qv;
-            if (r < nrow) {
-                const long src = (long(b) * T + t0 + r) * rs + long(h) * D + c * 8;
-                qv = *reinterpret_cast<const u32x4*>(q + src);
-                kv = *reinterpret_cast<const u32x4*>(k + src);
-                vv = *reinterpret_cast<const u32x4*>(v + src);
+            pq[u] = pk[u] = pv[u] = u32x4{0u, 0u, 0u, 0u};
+            if (r < nr) {
+                const long src = (long(b) * T + c0 + r) * rs + long(h) * D + c * 8;
+                pq[u] = *reinterpret_cast<const u32x4*>(q + src);
+                pk[u] = *reinterpret_cast<const u32x4*>(k + src);
+                pv[u] = *reinterpret_cast<const u32x4*>(v + src);
             }
-            Qs[r * CPR + (c ^ rswz<D>(r))] = qv;
-            Ks[r * CPR + (c ^ rswz<D>(r))] = kv;
-            Vs[r * CPR + (c ^ tswz<D>(r))] = vv;
+        }
+        if (wave == 0)
+            pg = (lane < nr) ? fmaxf(log_a[(long(b) * T + c0 + lane) * H + h], kLogAMin) : 0.0f;
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int x = tid + u * NT;
+            const int r = x / CPR;
+            const int c = x % CPR;
+            Qs[r * CPR + (c ^ rswz<D>(r))] = pq[u];
+            Ks[r * CPR + (c ^ rswz<D>(r))] = pk[u];
+            Vs[r * CPR + (c ^ tswz<D>(r))] = pv[u];
         }
         if (wave == 0) {
-            float g = (lane < nrow) ? fmaxf(log_a[(long(b) * T + t0 + lane) * H + h], kLogAMin)
-                                    : 0.0f;
+            float g = pg;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
                 const float y = __shfl_up(g, d, 64);
@@ -145,7 +180,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void linear_prefill_kernel(
             Gs[lane] = g;
             Es[lane] = __expf(g);
         }
-        __syncthreads();
+    };
+
+    const int nchunk = (T + kChunk - 1) / kChunk;
+    fetch(0);
+    stash();
+    share_state();
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        const int t0 = ch * kChunk;
+        const int nrow = min(kChunk, T - t0);
+        if (ch + 1 < nchunk) fetch(t0 + kChunk);          // in flight during this chunk
         // ---- w K: row j scaled by exp(G_last - G_j) ------------------------------------
         const float g_last = Gs[kChunk - 1];
         for (int x = tid; x < kChunk * CPR; x += NT) {
@@ -194,15 +239,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void linear_prefill_kernel(
         // ---- V operands of this wave's dims, k-steps c = 0..3 (P V and the update) ----
         bf16x8 vop[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) vop[c] = tr_operand(Vs, wave, c);
-        // ---- O = P V + exp(G_t) Q S0^T for both row tiles ------------------------------
-        bf16x8 sop[KK];                                   // S0^T as bf16 k operands
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sop[kk][i] = (__bf16)st[kk >> 1][(kk & 1) * 8 + i];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int c = 0; c < 4; ++c) vop[c] = tr_operand(Vs, dw, c);
+        // ---- O = P V + exp(G_t) Q S0^T for this wave's row tile -------------------------
+        {
+            const int tt = xw;
             const int tr = tt * 32 + (lane & 31);
             f32x16 oi = f32x16{}, ox = f32x16{};
 #pragma unroll
@@ -219,39 +259,44 @@ __global__ __launch_bounds__(64 * (D / 32)) void linear_prefill_kernel(
                 const bf16x4 hi = *reinterpret_cast<const bf16x4*>(
                     row + ((2 * kk + 1) ^ rswz<D>(tr)) * 8 + 4 * half);
                 const bf16x8 qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                ox = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sop[kk], ox, 0, 0, 0);
+                const bf16x8 sop = __builtin_bit_cast(bf16x8, Sb[(2 * kk + half) * D + dcol]);
+                ox = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sop, ox, 0, 0, 0);
             }
             // element e: row t = tt*32 + (e/4)*8 + h*4 + e%4, dim 32*wave + lane&31
+            uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D + dcol;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = tt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                if (t < nrow) {
-                    const float o = oi[e] + Es[t] * ox[e];
-                    out[(long(b) * T + t0 + t) * rs + long(h) * D + dcol] =
-                        __builtin_bit_cast(uint16_t, (__bf16)o);
-                }
+                const float o = oi[e] + Es[t] * ox[e];
+                if (nrow == kChunk || t < nrow)
+                    ob[long(t) * rs] = __builtin_bit_cast(uint16_t, (__bf16)o);
             }
         }
-        // ---- S^T = exp(G_last) S^T + (w K)^T V ----------------------------------------
+        // ---- S^T = exp(G_last) S^T + (w K)^T V for this wave's state tiles ------------
         const float decay = __expf(g_last);
 #pragma unroll
-        for (int kt = 0; kt < DT; ++kt) {
-            st[kt] *= decay;
+        for (int i = 0; i < KTW; ++i) {
+            st[i] *= decay;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bf16x8 wa = tr_operand(Ws, kt, c);
-                st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, vop[c], st[kt], 0, 0, 0);
+                const bf16x8 wa = tr_operand(Ws, xw * KTW + i, c);
+                st[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, vop[c], st[i], 0, 0, 0);
             }
         }
-        __syncthreads();                                  // the chunk's tiles are free
+        __syncthreads();                                  // the chunk's tiles and Sb are free
+        if (ch + 1 < nchunk) {
+            stash();
+            share_state();
+            __syncthreads();
+        }
     }
     float* so = state_out + long(bh) * D * D;
 #pragma unroll
-    for (int kt = 0; kt < DT; ++kt)
+    for (int i = 0; i < KTW; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int kr = kt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-            so[long(dcol) * D + kr] = st[kt][e];
+            const int kr = (xw * KTW + i) * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+            so[long(dcol) * D + kr] = st[i][e];
         }
 }
 
@@ -304,10 +349,10 @@ hipError_t launch_linear_prefill(int B, int H, int D, int64_t T, const uint16_t*
                                  hipStream_t st) {
     dim3 grid(unsigned(B * H));
     if (D == 128)
-        hipLaunchKernelGGL(linear_prefill_kernel<128>, grid, dim3(256), 0, st, int(T), H, q, k, v,
+        hipLaunchKernelGGL(linear_prefill_kernel<128>, grid, dim3(512), 0, st, int(T), H, q, k, v,
                            log_a, state_in, state_out, out);
     else
-        hipLaunchKernelGGL(linear_prefill_kernel<64>, grid, dim3(128), 0, st, int(T), H, q, k, v,
+        hipLaunchKernelGGL(linear_prefill_kernel<64>, grid, dim3(256), 0, st, int(T), H, q, k, v,
                            log_a, state_in, state_out, out);
     return hipGetLastError();
 }
