@@ -300,8 +300,10 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
         }
 }
 
-// One step: S <- a S + v k^T, o = S q.  One workgroup of 256 threads per
-// (batch, head); thread x owns D*D/256 consecutive elements of one row of S.
+// One step: S <- a S + v k^T, o = S q.  A workgroup of 256 threads takes 32
+// rows of one (batch, head)'s S (D/32 workgroups per head, so a step spreads
+// over enough waves to keep the state streaming); thread x owns 8 threads'
+// share, D/8 consecutive elements, of one row.
 template <int D>
 __global__ __launch_bounds__(256) void linear_step_kernel(int H, const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
@@ -309,32 +311,35 @@ __global__ __launch_bounds__(256) void linear_step_kernel(int H, const uint16_t*
                                                           const float* __restrict__ log_a,
                                                           float* __restrict__ state,
                                                           uint16_t* __restrict__ out) {
-    constexpr int PER = D * D / 256;                      // elements per thread
-    constexpr int TPR = D / PER;                          // threads per row
-    const int bh = blockIdx.x;
+    constexpr int RW = 32;                                // rows per workgroup
+    constexpr int TPR = 256 / RW;                         // threads per row
+    constexpr int PER = D / TPR;                          // elements per thread
+    const int bh = blockIdx.x / (D / RW);
     const int tid = threadIdx.x;
-    const int d = tid / TPR;                              // row of S (value dim)
+    const int d = (blockIdx.x % (D / RW)) * RW + tid / TPR;   // row of S (value dim)
     const int k0 = (tid % TPR) * PER;                     // first key dim
     const float a = __expf(fmaxf(log_a[bh], kLogAMin));
     const float vd = float(__builtin_bit_cast(__bf16, v[long(bh) * D + d]));
     float* srow = state + long(bh) * D * D + long(d) * D + k0;
     const uint16_t* kp = k + long(bh) * D + k0;
     const uint16_t* qp = q + long(bh) * D + k0;
+    float4 s4[PER / 4];
+#pragma unroll
+    for (int x = 0; x < PER / 4; ++x) s4[x] = *reinterpret_cast<const float4*>(srow + 4 * x);
     float acc = 0.0f;
 #pragma unroll
-    for (int x = 0; x < PER; x += 4) {
-        float4 s4 = *reinterpret_cast<const float4*>(srow + x);
-        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(kp + x);
-        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(qp + x);
-        s4.x = fmaf(a, s4.x, vd * float(k4[0]));
-        s4.y = fmaf(a, s4.y, vd * float(k4[1]));
-        s4.z = fmaf(a, s4.z, vd * float(k4[2]));
-        s4.w = fmaf(a, s4.w, vd * float(k4[3]));
-        acc = fmaf(s4.x, float(q4[0]), acc);
-        acc = fmaf(s4.y, float(q4[1]), acc);
-        acc = fmaf(s4.z, float(q4[2]), acc);
-        acc = fmaf(s4.w, float(q4[3]), acc);
-        *reinterpret_cast<float4*>(srow + x) = s4;
+    for (int x = 0; x < PER / 4; ++x) {
+        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(kp + 4 * x);
+        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(qp + 4 * x);
+        s4[x].x = fmaf(a, s4[x].x, vd * float(k4[0]));
+        s4[x].y = fmaf(a, s4[x].y, vd * float(k4[1]));
+        s4[x].z = fmaf(a, s4[x].z, vd * float(k4[2]));
+        s4[x].w = fmaf(a, s4[x].w, vd * float(k4[3]));
+        acc = fmaf(s4[x].x, float(q4[0]), acc);
+        acc = fmaf(s4[x].y, float(q4[1]), acc);
+        acc = fmaf(s4[x].z, float(q4[2]), acc);
+        acc = fmaf(s4[x].w, float(q4[3]), acc);
+        *reinterpret_cast<float4*>(srow + 4 * x) = s4[x];
     }
 #pragma unroll
     for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
@@ -360,7 +365,7 @@ hipError_t launch_linear_prefill(int B, int H, int D, int64_t T, const uint16_t*
 hipError_t launch_linear_step(int B, int H, int D, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const float* log_a, float* state, uint16_t* out,
                               hipStream_t st) {
-    dim3 grid(unsigned(B * H));
+    dim3 grid(unsigned(B * H * (D / 32)));
     if (D == 128)
         hipLaunchKernelGGL(linear_step_kernel<128>, grid, dim3(256), 0, st, H, q, k, v, log_a,
                            state, out);
