@@ -67,8 +67,8 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     __shared__ __align__(16) u32x4 Ws[kChunk * CPR];     // w_j K[j]
     __shared__ __align__(16) u32x4 Ps[kChunk * 8];       // P[t][j] bf16
     __shared__ __align__(16) u32x4 Sb[KK * 2 * D];       // S^T as bf16 k operands
-    __shared__ float Gs[kChunk];                          // G_t
-    __shared__ float Es[kChunk];                          // exp(G_t)
+    __shared__ __align__(16) float Gb[2][kChunk];         // G_t (two chunks)
+    __shared__ float Eb[2][kChunk];                       // exp(G_t)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -157,8 +157,21 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
                 pv[u] = *reinterpret_cast<const u32x4*>(v + src);
             }
         }
-        if (wave == 0)
-            pg = (lane < nr) ? fmaxf(log_a[(long(b) * T + c0 + lane) * H + h], kLogAMin) : 0.0f;
+        if (wave == NW - 1) pg = (lane < nr) ? log_a[(long(b) * T + c0 + lane) * H + h] : 0.0f;
+    };
+    // running sums of the fetched chunk's log a (clamped), by the last wave, into
+    // G buffer gbuf
+    auto scan_g = [&](int gbuf) {
+        if (wave == NW - 1) {
+            float g = fmaxf(pg, kLogAMin);
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float y = __shfl_up(g, d, 64);
+                if (lane >= d) g += y;
+            }
+            Gb[gbuf][lane] = g;
+            Eb[gbuf][lane] = __expf(g);
+        }
     };
     auto stash = [&]() {
 #pragma unroll
@@ -170,30 +183,25 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             Ks[r * CPR + (c ^ rswz<D>(r))] = pk[u];
             Vs[r * CPR + (c ^ tswz<D>(r))] = pv[u];
         }
-        if (wave == 0) {
-            float g = pg;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float y = __shfl_up(g, d, 64);
-                if (lane >= d) g += y;
-            }
-            Gs[lane] = g;
-            Es[lane] = __expf(g);
-        }
     };
 
     const int nchunk = (T + kChunk - 1) / kChunk;
     fetch(0);
     stash();
+    scan_g(0);
     share_state();
     __syncthreads();
     for (int ch = 0; ch < nchunk; ++ch) {
         const int t0 = ch * kChunk;
         const int nrow = min(kChunk, T - t0);
         if (ch + 1 < nchunk) fetch(t0 + kChunk);          // in flight during this chunk
+        const float* Gs = Gb[ch & 1];
+        const float* Es = Eb[ch & 1];
         // ---- w K: row j scaled by exp(G_last - G_j) ------------------------------------
         const float g_last = Gs[kChunk - 1];
-        for (int x = tid; x < kChunk * CPR; x += NT) {
+        // (with 8 waves by waves 4-7, which take no q.k tile; with 4 by all)
+        constexpr int WW0 = NW > 4 ? 4 : 0;
+        for (int x = tid - WW0 * 64; x >= 0 && x < kChunk * CPR; x += NT - WW0 * 64) {
             const int r = x / CPR;
             const float wj = __expf(g_last - Gs[r]);
             const int pc = x % CPR;                       // physical chunk of Ks row r
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             Ws[r * CPR + (c ^ tswz<D>(r))] = __builtin_bit_cast(u32x4, wv);
         }
         // ---- P^T = K Q^T for the tiles (jt, tt) of this wave; mask, decay, to LDS ----
-        for (int tile = wave; tile < 4; tile += NW) {
+        for (int tile = wave; tile < 4; tile += 4) {
             const int jt = tile & 1;
             const int tt = tile >> 1;
             f32x16 sacc = f32x16{};
@@ -219,12 +227,26 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
                     bf16x8, Qs[tr * CPR + ((2 * kk + half) ^ rswz<D>(tr))]);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, sacc, 0, 0, 0);
             }
+            // operands two k-steps ahead of the MFMA that takes them
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+            for (int x = 0; x < KK - 2; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
             const float gt = Gs[tr];
+            // G of this lane's keys: 4 runs of 4 consecutive rows
+            float4 gj[4];
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                gj[e4] = *reinterpret_cast<const float4*>(&Gs[jt * 32 + e4 * 8 + half * 4]);
             bf16x8 pf[2];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int j = jt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                const float p = (j <= tr) ? sacc[e] * __expf(gt - Gs[j]) : 0.0f;
+                const float g4[4] = {gj[e >> 2].x, gj[e >> 2].y, gj[e >> 2].z, gj[e >> 2].w};
+                const float p = (j <= tr) ? sacc[e] * __expf(gt - g4[e & 3]) : 0.0f;
                 pf[e >> 3][e & 7] = (__bf16)p;
             }
             // P row tr, k-step c = 2jt + s, lane-half h: chunk 2c + h
@@ -262,6 +284,14 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
                 const bf16x8 sop = __builtin_bit_cast(bf16x8, Sb[(2 * kk + half) * D + dcol]);
                 ox = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sop, ox, 0, 0, 0);
             }
+            // operands (two q halves, one state piece) two k-steps ahead
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 2);
+#pragma unroll
+            for (int x = 0; x < KK - 2; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x100, 3, 2);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
             // element e: row t = tt*32 + (e/4)*8 + h*4 + e%4, dim 32*wave + lane&31
             uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D + dcol;
 #pragma unroll
@@ -283,6 +313,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
                 st[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, vop[c], st[i], 0, 0, 0);
             }
         }
+        if (ch + 1 < nchunk) scan_g((ch + 1) & 1);       // the next chunk's G, other buffer
         __syncthreads();                                  // the chunk's tiles and Sb are free
         if (ch + 1 < nchunk) {
             stash();
