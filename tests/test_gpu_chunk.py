@@ -245,3 +245,22 @@ def test_chunk_full_size():
     st.prefill([inp["T"]] * wl.B)
     st.chunk(504)
     st.decode(8)
+
+
+@pytest.mark.parametrize("s,C", [(0, 12), (3, 0)])
+def test_chunk_no_sink_or_no_segment(s, C):
+    """No sink (the CNN's left padding is reached) or capacity 0 (no segment rows)."""
+    st = Stream(2, 4, 2, 64, s, 16, C, 200, seed=55 + s, b2=0.05)
+    st.prefill([60, 90])
+    st.chunk(37)
+    st.decode(6)
+    st.chunk(25)
+
+
+def test_long_chunk():
+    """A chunk of 300 tokens, far longer than w + C: most of it leaves the window inside the
+    call and the segment overflows repeatedly (G1, D64)."""
+    st = Stream(1, 2, 2, 64, 2, 24, 10, 500, seed=57, b2=0.02)
+    st.prefill([90])
+    st.chunk(300)
+    st.decode(5)
