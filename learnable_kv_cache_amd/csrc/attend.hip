@@ -102,7 +102,8 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     __shared__ __align__(16) uint32_t lst[kMaxList];
     __shared__ __align__(16) int32_t brank[kBr];
     __shared__ int lfull[kMaxList / 64];            // list block visible to every row of the tile
-    __shared__ int wsum[NW];
+    __shared__ int wcnt[64];                        // per (pass slot, wave) counts
+    __shared__ int woff[65];                        // their exclusive prefix, then the total
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -193,11 +194,26 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         }                                                                                  \
     }
 
-    // ranks of the first kBr band keys: a band key j can be a retained column
-    // of a row of the tile only if j <= i_last - w <= band_lo + P - 2
-    for (int t = tid; t < kBr; t += NW * 64) {
-        const int j = band_lo + t;
-        brank[t] = (j < s) ? -1 : ((j <= band_hi) ? rk[j] : kNotCand);   // sink always passes
+    // ---- prologue: every global load first, then the LDS work ----------------------
+    constexpr int NT = NW * 64;
+    constexpr int LU = 8;                         // list candidates per thread and pass
+    static_assert(LU * NW == 64, "one wave scans the per-(pass slot, wave) counts");
+    const int ns = min(s, band_lo);               // sink tokens below the band
+    const int thr0 = (band_lo > 0) ? th[i0 - w] : -2;    // list threshold at the first row
+    const int thr_last = (band_lo > 0) ? th[i_last - w] : -2;
+    // rank of band key band_lo + tid: a band key j can be a retained column of a
+    // row of the tile only if j <= i_last - w <= band_lo + P - 2
+    int brv = kNotCand;
+    if (tid < kBr) {
+        const int j = band_lo + tid;
+        brv = (j < s) ? -1 : ((j <= band_hi) ? rk[j] : kNotCand);    // sink always passes
+    }
+    // list candidates j = s + u*NT + tid of the first pass (coalesced)
+    int rr[LU];
+#pragma unroll
+    for (int u = 0; u < LU; ++u) {
+        const int j = s + u * NT + tid;
+        rr[u] = (j < band_lo) ? rk[j] : kNotCand;
     }
 
     // ---- this lane's query row --------------------------------------------------
@@ -220,56 +236,58 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const uint32_t lim = (uint32_t(min(max(thr_row + 1, 0), 0xfffe)) << 16) | 0xffffu;
     const float csc = kLog2e * rsqrtf(float(D));
 
-    // ---- gathered columns below the band: sink, then retained tokens ----------
-    int len = 0;
-    if (band_lo > 0) {
-        const int thr0 = th[i0 - w];
-        const int ns = min(s, band_lo);
-        for (int j = tid; j < ns; j += NW * 64) lst[j] = uint32_t(j);     // field 0: always visible
-        len = ns;
-        // candidates j in [s, band_lo) alive at the first row, in index order
-        for (int base = s; base < band_lo; base += NW * 64 * 16) {
-            const int j0 = base + tid * 16;
-            int rr[16];
-            int cnt = 0;
+    if (tid < kBr) brank[tid] = brv;
+    // ---- gathered columns below the band: sink, then the candidates alive at the
+    //      tile's first row, in index order (ballot compaction: order by pass slot
+    //      u, then wave, then lane, which is index order) ------------------------------
+    int len = ns;
+    for (int j = tid; j < ns; j += NT) lst[j] = uint32_t(j);           // field 0: always visible
+    for (int base = s; base < band_lo; base += LU * NT) {
+        if (base != s) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                rr[u] = (j0 + u < band_lo) ? rk[j0 + u] : kNotCand;
-                cnt += (rr[u] <= thr0) ? 1 : 0;
+            for (int u = 0; u < LU; ++u) {
+                const int j = base + u * NT + tid;
+                rr[u] = (j < band_lo) ? rk[j] : kNotCand;
             }
-            // block exclusive scan of cnt
-            int incl = cnt;
+        }
+        uint32_t pre[LU];
+#pragma unroll
+        for (int u = 0; u < LU; ++u) {
+            const unsigned long long m = __ballot(rr[u] <= thr0);
+            pre[u] = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+            if (lane == 0) wcnt[u * NW + wave] = __popcll(m);
+        }
+        __syncthreads();
+        if (wave == 0) {                          // exclusive scan of the 64 counts
+            const int c = wcnt[lane];
+            int incl = c;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
-                int y = __shfl_up(incl, d, 64);
+                const int y = __shfl_up(incl, d, 64);
                 if (lane >= d) incl += y;
             }
-            if (lane == 63) wsum[wave] = incl;
-            __syncthreads();
-            int woff = 0, tot = 0;
-#pragma unroll
-            for (int x = 0; x < NW; ++x) {
-                woff += (x < wave) ? wsum[x] : 0;
-                tot += wsum[x];
-            }
-            int o = len + woff + incl - cnt;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                if (rr[u] <= thr0) lst[o++] = (uint32_t(rr[u] + 1) << 16) | uint32_t(j0 + u);
-            }
-            len += tot;
-            __syncthreads();
+            woff[lane] = incl - c;
+            if (lane == 63) woff[64] = incl;
         }
-        // pad to whole blocks with entries no row sees (field 0xffff, key 0)
-        for (int e = len + tid; e < ((len + 63) & ~63); e += NW * 64) lst[e] = 0xffff0000u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < LU; ++u) {
+            if (rr[u] <= thr0)
+                lst[len + woff[u * NW + wave] + int(pre[u])] =
+                    (uint32_t(rr[u] + 1) << 16) | uint32_t(base + u * NT + tid);
+        }
+        len += woff[64];
+        __syncthreads();                          // wcnt and woff are reused
     }
+    // pad to whole blocks with entries no row sees (field 0xffff, key 0)
+    for (int e = len + tid; e < ((len + 63) & ~63); e += NT) lst[e] = 0xffff0000u;
     const int nlist = (len + 63) / 64;
     const int nblk = nband + nlist;
     __syncthreads();                              // list complete
     // thr is non-increasing, so the tile's last row has the strictest list
     // threshold: a block whose entries all pass it needs no mask
     if (nlist > 0) {
-        const int thr_last = th[i_last - w];
         const uint32_t lim_last = (uint32_t(min(max(thr_last + 1, 0), 0xfffe)) << 16) | 0xffffu;
         for (int bl = wave; bl < nlist; bl += NW) {
             const bool ok = lst[bl * 64 + lane] <= lim_last;
