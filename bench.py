@@ -49,8 +49,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -452,8 +452,9 @@ def main():
     ncand = views["ncand"].cpu().numpy()
     cand_rate = ncand / max(1, T - wl.window - wl.sink)
 
-    pf_ms = float(np.mean(prefill_ms))
-    att_ms = float(np.mean(stage_ms["attend"]))
+    # medians over the timed steps
+    pf_ms = float(np.median(prefill_ms))
+    att_ms = float(np.median(stage_ms["attend"]))
     achieved = attn_flops / (att_ms * 1e-3)
     attend_src = os.path.join(ROOT, "learnable_kv_cache_amd", "csrc", "attend.hip")
     traffic = measured_traffic("attend_prefill", attend_src)
@@ -462,14 +463,14 @@ def main():
                 "frac": achieved / PEAK_BF16_FLOPS, "traffic": traffic,
                 "flops_per_launch": attn_flops, "ms_per_launch": att_ms}
     kv_bytes = 2 * B * T * wl.Hkv * wl.D * 2
-    score_ms = float(np.mean(stage_ms["score"]))
+    score_ms = float(np.median(stage_ms["score"]))
     stages = {
         "score": {"ms": score_ms, "bound": "hbm",
                   "achieved_GBps": kv_bytes / (score_ms * 1e-3) / 1e9,
                   "frac": kv_bytes / (score_ms * 1e-3) / PEAK_HBM_BPS},
-        "select": {"ms": float(np.mean(stage_ms["select"]))},
+        "select": {"ms": float(np.median(stage_ms["select"]))},
         "attend": {"ms": att_ms, "frac_mfma": achieved / PEAK_BF16_FLOPS},
-        "build_cache": {"ms": float(np.mean(stage_ms["build_cache"]))},
+        "build_cache": {"ms": float(np.median(stage_ms["build_cache"]))},
     }
     result = {
         "metric": METRIC,
@@ -503,8 +504,8 @@ def main():
         nvis = float(counts.mean()) + wl.window + wl.sink
         step_bytes = (B * wl.Hkv * nvis * wl.D * 2 * 2 + 2 * B * wl.Hq * wl.D * 2
                       + 2 * B * wl.Hkv * wl.D * 2 + B * wl.Hkv * wl.capacity * 4)
-        us_rot = float(np.mean(dec_rot_ms)) * 1e3 / (ndec * L)
-        us_warm = float(np.mean(dec_warm_ms)) * 1e3 / ndec
+        us_rot = float(np.median(dec_rot_ms)) * 1e3 / (ndec * L)
+        us_warm = float(np.median(dec_warm_ms)) * 1e3 / ndec
         achieved_b = step_bytes / (us_rot * 1e-6)
         result["decode"] = {
             "us_per_step": us_rot, "warm_single_cache_us_per_step": us_warm,
