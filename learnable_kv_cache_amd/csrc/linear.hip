@@ -68,7 +68,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     __shared__ __align__(16) u32x4 Ps[kChunk * 8];       // P[t][j] bf16
     __shared__ __align__(16) u32x4 Sb[KK * 2 * D];       // S^T as bf16 k operands
     __shared__ __align__(16) float Gb[2][kChunk];         // G_t (two chunks)
-    __shared__ float Eb[2][kChunk];                       // exp(G_t)
+    __shared__ __align__(16) float Eb[2][kChunk];         // exp(G_t)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -294,10 +294,15 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
             // element e: row t = tt*32 + (e/4)*8 + h*4 + e%4, dim 32*wave + lane&31
             uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D + dcol;
+            float4 ev[4];                                 // exp(G_t) of this lane's rows
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                ev[e4] = *reinterpret_cast<const float4*>(&Es[tt * 32 + e4 * 8 + half * 4]);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = tt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                const float o = oi[e] + Es[t] * ox[e];
+                const float e4v[4] = {ev[e >> 2].x, ev[e >> 2].y, ev[e >> 2].z, ev[e >> 2].w};
+                const float o = oi[e] + e4v[e & 3] * ox[e];
                 if (nrow == kChunk || t < nrow)
                     ob[long(t) * rs] = __builtin_bit_cast(uint16_t, (__bf16)o);
             }
