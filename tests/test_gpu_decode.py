@@ -181,3 +181,47 @@ def test_fused_step_equals_evict_then_attend():
     # ring scores: NaN where unscored on both sides
     assert torch.equal(torch.nan_to_num(va["ring_score"], nan=-1.0),
                        torch.nan_to_num(vb["ring_score"], nan=-1.0))
+
+
+def test_decode_from_empty_cache():
+    """No prefill: a freshly initialised cache stepped from pos 0 (sink, ring and segment
+    filled by decode alone; deferred batches fire from the first tokens on)."""
+    B, n, Hq, Hkv, D, s, w, C = 2, 60, 4, 2, 64, 3, 8, 4
+    q, k, v, cnn = synth.random_case(41, B, n, Hq, Hkv, D, b2=0.05)
+    G = Hq // Hkv
+    layer = lte.Layer(lte.Config(B, Hq, Hkv, D, s, w, C))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    dcnn = lte.CNN(cnn)
+    ws = layer.alloc_workspace(0)
+    cache = layer.alloc_cache()
+    views = layer.cache_views(cache)
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    r_all = oracle.cnn_scores(kn, vn, cnn["W1"], cnn["b1"], cnn["W2"], cnn["b2"])
+    oc = oracle.LayerCache(B, Hkv, D, s, w, C, cnn=cnn)
+    for t in range(n):
+        o_t = layer.decode_step(qd[:, t].contiguous(), kd[:, t].contiguous(),
+                                vd[:, t].contiguous(), dcnn, cache, ws)
+        oc.ingest(kn[:, t], vn[:, t])
+        torch.cuda.synchronize()
+        assert np.all(views["pos"].cpu().numpy() == t + 1)
+        assert int(views["flags"].cpu().numpy().max()) == 0
+        o_g = o_t.float().cpu().numpy()
+        count = views["count"].cpu().numpy()
+        ret_idx = views["ret_idx"].cpu().numpy()
+        for b in range(B):
+            for g in range(Hkv):
+                gset = set(ret_idx[b, g, :count[b, g]].tolist())
+                oset = set(oc.retained_indices(b, g).tolist())
+                cut = min(float(r_all[b, g, j]) for j in oset) if len(oset) == C else None
+                for j in gset ^ oset:
+                    rj = float(r_all[b, g, j])
+                    assert abs(rj - 0.5) <= BAND or (cut is not None and abs(rj - cut) <= BAND)
+                idx = np.array(sorted(set(range(min(s, t + 1))) | set(range(max(0, t - w + 1), t + 1))
+                                      | gset), np.int64)
+                ref = _attend_on_set(qn[b, t, g * G:(g + 1) * G], kn[b, :, g], vn[b, :, g], idx, G)
+                d = np.abs(o_g[b, g * G:(g + 1) * G] - ref)
+                # over the first few keys the output is not averaged down to a small
+                # magnitude, so its bf16 rounding (unit roundoff 2^-8, on the output and
+                # on the probabilities) adds a term proportional to the output itself
+                mean_tol = MEAN_ABS + 2.0 ** -8 * float(np.abs(ref).mean())
+                assert d.max() <= MAX_ABS and d.mean() <= mean_tol, (t, b, g, d.mean())
