@@ -46,6 +46,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max of x over lanes l and l ^ 32, by one cross-half swap (no LDS round trip)
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // LDS chunk swizzle of tile row r (a key): the 16-byte chunk c of row r is
 // stored at chunk position c ^ swz(r).  Two access patterns must spread over
 // the banks: the K operand reads one chunk of 8 (or 16) consecutive rows, the
@@ -425,7 +437,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[ks][e]);
-        const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const float mrow = max_xor32(mloc);
         // NaN (both -inf: nothing visible yet) compares false: no move
         const bool move = (mrow - m_run) * csc > 8.0f;
         if (__ballot(move) != 0ull) {
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
 #undef LTE_STORE
 
     // ---- normalise and store: element e of d-tile dt is dim dt*32 + (e/4)*8 + half*4 + e%4
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = add_xor32(l_run);
     if (row_ok) {
         const float inv = 1.0f / l_tot;
         uint16_t* orow = out + ((long(b) * qrows + (i_row - qlo)) * Hq + h) * D;
