@@ -8,8 +8,11 @@
 // (the layer's input dtype), W1 is rounded to bf16, accumulation is fp32; the
 // GELU, the 96-term second layer and the sigmoid run in fp32.
 //
-// Grid: one workgroup per 124 consecutive tokens of one (batch, KV head).
-// Tokens outside [0, T_b) read as zero (first layer's padding) and their hidden
+// Grid: a few workgroups of 8 waves per (batch, KV head), each over a
+// contiguous run of 224-token chunks (8 waves x 28 tokens), with the head's W1
+// staged in LDS once.  Two workgroups fit a CU (16 waves), which hide each
+// other's load latency.  Tokens
+// outside [0, T_b) read as zero (first layer's padding) and their hidden
 // activations are zero (second layer's padding); T_b is the sequence's length
 // (seq_lens[b], or T for every sequence).  With score_lo (per (b, g)), rows
 // below it are not written: they hold scores already known.
@@ -38,46 +41,54 @@ __global__ void pack_w1_kernel(int Hkv, int D, const float* __restrict__ w1,
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void score_prefill_kernel(
-    int T, int Hkv, int ntile, const int32_t* __restrict__ seq_lens,
+__global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_eu(4))) void score_prefill_kernel(
+    int T, int Hkv, int nchunk, int nsplit, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ score_lo, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v,
     const bf16x8* __restrict__ w1p, const float* __restrict__ b1, const float* __restrict__ w2,
     const float* __restrict__ b2, float* __restrict__ scores) {
-    __shared__ __align__(16) unsigned char buf[ScoreSmem<D>::kBytes];
-    __shared__ float w2s[kHidden * 3];
     constexpr int NW = ScoreSmem<D>::NW;
+    __shared__ bf16x8 wl[NW];
+    __shared__ float w2s[kHidden * 3];
+    __shared__ float act[kScoreWaves][kActRows * kActPitch];
 
     const int tid = threadIdx.x;
-    const int bg = blockIdx.x / ntile;
-    const int tile = blockIdx.x % ntile;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int bg = blockIdx.x / nsplit;
+    const int part = blockIdx.x % nsplit;
     const int b = bg / Hkv;
     const int g = bg % Hkv;
-    const int t0 = tile * kScoreTile;
     const int Tb = seq_len_of(seq_lens, b, T);
-    if (t0 >= Tb) return;                                    // the whole tile is padding
     const int lo = score_lo ? score_lo[bg] : 0;              // rows below keep their scores
-    if (t0 + kScoreTile <= lo) return;
+    // this workgroup's chunks, without those wholly past T_b or below lo
+    const int per = (nchunk + nsplit - 1) / nsplit;
+    const int c_begin = max(part * per, lo / kChunkTokens);
+    const int c_end = min(min(nchunk, (part + 1) * per), (Tb + kChunkTokens - 1) / kChunkTokens);
+    if (c_begin >= c_end) return;
 
-    bf16x8* wl = reinterpret_cast<bf16x8*>(buf);
     const bf16x8* wsrc = w1p + long(g) * NW;
-    for (int x = tid; x < NW; x += 256) wl[x] = wsrc[x];
-    for (int x = tid; x < kHidden * 3; x += 256) w2s[x] = w2[g * kHidden * 3 + x];
+    for (int x = tid; x < NW; x += 64 * kScoreWaves) wl[x] = wsrc[x];
+    for (int x = tid; x < kHidden * 3; x += 64 * kScoreWaves) w2s[x] = w2[g * kHidden * 3 + x];
+    const float b1o = b1[g * kHidden + (lane & 31)];
+    const float b2g = b2[g];
 
     const long row_stride = long(Hkv) * D;
     const uint16_t* kb = k + (long(b) * T * Hkv + g) * D;
     const uint16_t* vb = v + (long(b) * T * Hkv + g) * D;
     float* out = scores + long(bg) * T;
-    score_chunk<D>(
-        buf, w2s, b1 + g * kHidden, b2[g], t0, 0, Tb - 1,
-        [&](int x, const uint16_t*& kp, const uint16_t*& vp) {
-            if (x < 0 || x >= Tb) return false;
-            kp = kb + long(x) * row_stride;
-            vp = vb + long(x) * row_stride;
-            return true;
-        },
-        [&](int x) { return x < 0 || x >= Tb; },
-        [&](int t, float r) { if (t >= lo) out[t] = r; });
+    __syncthreads();                                         // W1 and W2 staged
+    float* my_act = act[wave];
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0 = c * kChunkTokens + wave * kPassTokens;
+        const int tok = t0 - 2 + (lane & 31);                // this lane's row
+        const bool ok = tok >= 0 && tok < Tb;
+        score_pass<D>(
+            wl, w2s, b1o, b2g, kb + long(tok) * row_stride, vb + long(tok) * row_stride, ok,
+            my_act, t0, 0, Tb - 1,
+            [&](int x) { return x < 0 || x >= Tb; },
+            [&](int t, float r) { if (t >= lo) out[t] = r; });
+    }
 }
 
 }  // namespace
@@ -95,15 +106,23 @@ hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_l
                                 const int32_t* score_lo, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* w1p, const lte_cnn& cnn, float* scores,
                                 hipStream_t st) {
-    const int ntile = int((T + kScoreTile - 1) / kScoreTile);
-    dim3 grid(unsigned(long(sh.B) * sh.Hkv * ntile));
+    // about two workgroups per CU over the whole grid (256 CUs), each (b, g)
+    // split into nsplit runs of chunks
+    const int nchunk = int((T + kChunkTokens - 1) / kChunkTokens);
+    const long bgs = long(sh.B) * sh.Hkv;
+    long nsplit = (512 + bgs - 1) / bgs;
+    if (nsplit > nchunk) nsplit = nchunk;
+    if (nsplit < 1) nsplit = 1;
+    dim3 grid(unsigned(bgs * nsplit));
     const bf16x8* wp = reinterpret_cast<const bf16x8*>(w1p);
     if (sh.D == 128) {
-        hipLaunchKernelGGL(score_prefill_kernel<128>, grid, dim3(256), 0, st, int(T), sh.Hkv,
-                           ntile, seq_lens, score_lo, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+        hipLaunchKernelGGL(score_prefill_kernel<128>, grid, dim3(64 * kScoreWaves), 0, st, int(T), sh.Hkv,
+                           nchunk, int(nsplit), seq_lens, score_lo, k, v, wp, cnn.b1, cnn.w2,
+                           cnn.b2, scores);
     } else {
-        hipLaunchKernelGGL(score_prefill_kernel<64>, grid, dim3(256), 0, st, int(T), sh.Hkv,
-                           ntile, seq_lens, score_lo, k, v, wp, cnn.b1, cnn.w2, cnn.b2, scores);
+        hipLaunchKernelGGL(score_prefill_kernel<64>, grid, dim3(64 * kScoreWaves), 0, st, int(T), sh.Hkv,
+                           nchunk, int(nsplit), seq_lens, score_lo, k, v, wp, cnn.b1, cnn.w2,
+                           cnn.b2, scores);
     }
     return hipGetLastError();
 }

@@ -7,8 +7,10 @@
 // token is computable once its receptive field (tokens j-2 .. j+2 for two
 // kernel-3 layers) is present.
 //
-// score_chunk: one workgroup of 256 threads (4 waves) scores the 124 tokens
-// [t0, t0+124) (prefill).  score_wave: one wave scores 28 tokens (decode).  Layer 1 is written as Y_tap = W1[:, :, tap] . x per token
+// score_pass: one wave of a prefill workgroup scores 28 tokens from A
+// fragments it already holds, with W1 staged once per workgroup in LDS.
+// score_wave: one wave scores 28 tokens (decode), W1 read from global memory.
+// Layer 1 is written as Y_tap = W1[:, :, tap] . x per token
 // (v_mfma_f32_32x32x16_bf16, 32 tokens x 96 outputs per wave), then
 // h[j] = b1 + Y_0[j-1] + Y_1[j] + Y_2[j+1].
 #pragma once
@@ -17,18 +19,38 @@
 
 namespace lte {
 
-constexpr int kScoreTile = 124;        // scored tokens per workgroup call
-constexpr int kScoreRows = 128;        // tokens whose Y a call computes
+constexpr int kPassTokens = 28;      // tokens one wave scores per pass (32 rows with halos)
+constexpr int kScoreWaves = 8;       // waves of a prefill scoring workgroup
+constexpr int kChunkTokens = kScoreWaves * kPassTokens;   // per prefill workgroup pass
+constexpr int kActPitch = 33;        // floats per activation row in LDS (bank spread)
+constexpr int kActRows = 30;         // rows 1 .. 30 of a pass feed its scores
 
 template <int D>
 struct ScoreSmem {
     static constexpr int KK = (2 * D) / 16;          // MFMA k-steps over the 2D channels
     static constexpr int NW = 3 * KK * 64;           // bf16x8 entries of one head's packed W1
-    static constexpr int kBytes = (NW * 16 > kScoreRows * 96 * 4) ? NW * 16 : kScoreRows * 96 * 4;
 };
 
+// erf by Abramowitz and Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
+// exp(-x^2) with t = 1 / (1 + p x), absolute error at most 1.5e-7; erf is odd.
+// Branch-free: one reciprocal, one exponential, five FMAs.
+constexpr float kErfP = 0.3275911f;
+constexpr float kErfA1 = 0.254829592f;
+constexpr float kErfA2 = -0.284496736f;
+constexpr float kErfA3 = 1.421413741f;
+constexpr float kErfA4 = -1.453152027f;
+constexpr float kErfA5 = 1.061405429f;
+__device__ __forceinline__ float erf_as(float x) {
+    const float ax = fabsf(x);
+    const float t = 1.0f / fmaf(kErfP, ax, 1.0f);
+    const float poly =
+        t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, kErfA5, kErfA4), kErfA3), kErfA2), kErfA1);
+    return copysignf(1.0f - poly * __expf(-ax * ax), x);
+}
+
 __device__ __forceinline__ float gelu_erf(float h) {
-    return 0.5f * h * (1.0f + erff(h * 0.70710678118654752f));
+    return 0.5f * h * (1.0f + erf_as(h * 0.70710678118654752f));
 }
 
 // Packed-W1 entry index x (bf16x8 units) -> (tap, kk, lane); element e of the
@@ -39,110 +61,109 @@ __device__ __forceinline__ void w1p_coords(int x, int KK, int& tap, int& kk, int
     tap = x / (64 * KK);
 }
 
-// Scores tokens [t0, t0+124) clipped to [tlo, thi] and hands each to store(t, r).
-//   buf      LDS of ScoreSmem<D>::kBytes, already holding this head's packed W1
-//   w2s      LDS copy of this head's W2 [32][3]
-//   x_row(x, kp, vp) -> true and row pointers of token x, or false: x reads as 0
-//   a_zero(x)        -> true where layer 2 sees zero padding (outside the sequence)
-// Ends with the LDS buffer overwritten (holds Y); callers re-stage W1 to reuse it.
-template <int D, class XRow, class AZero, class Store>
-__device__ __forceinline__ void score_chunk(unsigned char* buf, const float* w2s,
-                                            const float* __restrict__ b1g, float b2g, int t0,
-                                            int tlo, int thi, XRow x_row, AZero a_zero,
-                                            Store store) {
+// x held by lane l ^ 32 (one cross-half swap)
+__device__ __forceinline__ float other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    // first: every lane's copy of the low half's x; second: of the high half's
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Scores tokens [t0, t0+28) clipped to [tlo, thi] and hands each to store(t, r).
+//   wl       this head's packed W1 in LDS
+//   w2s      this head's W2 [32][3] in LDS
+//   b1o      b1 of output column lane % 32
+//   kp, vp   k and v row of this lane's token (row lane % 32: token t0 - 2 + lane % 32), if ok;
+//            the A operand of k-step kk is channels 16 kk + 8 (lane/32) .. +8 of concat(k, v)
+//   act      wave-private LDS tile [kActRows][kActPitch]: hidden activations of rows 1 .. 30
+//   a_zero(x) -> true where layer 2 sees zero padding (outside the sequence)
+// The accumulator element e of lane l holds row 8 (e/4) + 4 (l/32) + e%4 and
+// output column l % 32, so a row's neighbours are in the same lane except
+// across groups of 4 rows, where they sit in lane l ^ 32.
+template <int D, class AZero, class Store>
+__device__ __forceinline__ void score_pass(const bf16x8* wl, const float* w2s, float b1o,
+                                           float b2g, const uint16_t* kp, const uint16_t* vp,
+                                           bool ok, float* act, int t0, int tlo, int thi,
+                                           AZero a_zero, Store store) {
     constexpr int KK = ScoreSmem<D>::KK;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const bf16x8* wl = reinterpret_cast<const bf16x8*>(buf);
-
-    // A operands: token (lane % 32) of this wave's 32, channels 16 kk + 8 (lane/32) .. +8
-    const int tok = t0 - 2 + wave * 32 + (lane & 31);
-    const uint16_t* kp = nullptr;
-    const uint16_t* vp = nullptr;
-    const bool ok = x_row(tok, kp, vp);
-    bf16x8 afrag[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        const int c = kk * 16 + (lane >> 5) * 8;
-        if (ok) {
-            const uint16_t* src = (c < D) ? (kp + c) : (vp + (c - D));
-            afrag[kk] = *reinterpret_cast<const bf16x8*>(src);
-        } else {
-            afrag[kk] = bf16x8{};
-        }
-    }
-    __syncthreads();                                  // W1 staged by the caller
-
+    constexpr int KH = KK / 2;                       // k-steps per operand half
+    const int lane = threadIdx.x & 63;
+    const bool hi = (lane & 32) != 0;
     f32x16 acc[3];
 #pragma unroll
     for (int tp = 0; tp < 3; ++tp) acc[tp] = f32x16{};
+    // the A operands in two halves of the channels, to keep registers for
+    // four waves per SIMD
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 afrag[KH];
 #pragma unroll
-        for (int tp = 0; tp < 3; ++tp) {
-            const bf16x8 bfrag = wl[(tp * KK + kk) * 64 + lane];
-            acc[tp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[kk], bfrag, acc[tp], 0, 0, 0);
+        for (int q = 0; q < KH; ++q) {
+            const int ch = (hf * KH + q) * 16 + (lane >> 5) * 8;
+            afrag[q] = ok ? *reinterpret_cast<const bf16x8*>((ch < D) ? (kp + ch) : (vp + (ch - D)))
+                          : bf16x8{};
         }
-    }
-    __syncthreads();                                  // W1 no longer read: reuse for Y
-
-    // accumulator element e of lane l: row (token) 8 (e/4) + 4 (l/32) + e%4,
-    // column (output) l % 32
-    float* Y = reinterpret_cast<float*>(buf);         // [128][96]
 #pragma unroll
-    for (int tp = 0; tp < 3; ++tp) {
+        for (int q = 0; q < KH; ++q) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = wave * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-            Y[row * 96 + tp * 32 + (lane & 31)] = acc[tp][e];
+            for (int tp = 0; tp < 3; ++tp) {
+                const bf16x8 bfrag = wl[(tp * KK + hf * KH + q) * 64 + lane];
+                acc[tp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[q], bfrag, acc[tp], 0, 0, 0);
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-
-    // hidden layer for local rows 1..126 (tokens t0-1 .. t0+124).  GELU(h) of
-    // row r overwrites Y_1 of row r: that element is read by this thread only.
-    for (int x = tid; x < (kScoreRows - 2) * kHidden; x += 256) {
-        const int r = x / kHidden + 1;
-        const int o = x % kHidden;
-        const int t = t0 - 2 + r;
-        float a = 0.0f;
-        if (!a_zero(t)) {
-            const float h = b1g[o] + Y[(r - 1) * 96 + o] + Y[r * 96 + 32 + o] +
-                            Y[(r + 1) * 96 + 64 + o];
-            a = gelu_erf(h);
-        }
-        Y[r * 96 + 32 + o] = a;
+    // tap 0 of row-1 and tap 2 of row+1 where they sit in the other lane half
+    float p0[4], p2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p0[i] = other_half(acc[0][4 * i + 3]);
+        p2[i] = other_half(acc[2][4 * i]);
     }
-    __syncthreads();
-
-    // output layer + sigmoid for tokens t0 .. t0+123 (local rows 2 .. 125)
-    if (tid < kScoreTile) {
-        const int t = t0 + tid;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int i = e >> 2;
+        const int j = e & 3;
+        const int row = 8 * i + (hi ? 4 : 0) + j;
+        // rows 0 and 31 (the outer halo) take no neighbour: they feed no score
+        const float y0 = (j > 0) ? acc[0][e - 1] : (hi ? p0[i] : (i > 0 ? p0[i - 1] : 0.0f));
+        const float y2 = (j < 3) ? acc[2][e + 1] : (hi ? (i < 3 ? p2[i + 1] : 0.0f) : p2[i]);
+        const float h = b1o + y0 + acc[1][e] + y2;
+        if (row >= 1 && row <= kActRows)
+            act[(row - 1) * kActPitch + (lane & 31)] = a_zero(t0 - 2 + row) ? 0.0f : gelu_erf(h);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // output layer + sigmoid for tokens t0 .. t0+27 (rows 2 .. 29)
+    if (lane < kPassTokens) {
+        const int t = t0 + lane;
         if (t >= tlo && t <= thi) {
             float z = b2g;
-            const float* a = Y + 32;
-            const int r = tid + 2;
+            const int r = lane + 1;                          // act row of token t
 #pragma unroll 8
             for (int o = 0; o < kHidden; ++o) {
-                z += w2s[o * 3 + 0] * a[(r - 1) * 96 + o] + w2s[o * 3 + 1] * a[r * 96 + o] +
-                     w2s[o * 3 + 2] * a[(r + 1) * 96 + o];
+                z += w2s[o * 3 + 0] * act[(r - 1) * kActPitch + o] +
+                     w2s[o * 3 + 1] * act[r * kActPitch + o] +
+                     w2s[o * 3 + 2] * act[(r + 1) * kActPitch + o];
             }
             store(t, 1.0f / (1.0f + expf(-z)));
         }
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // One wave scores tokens [t0, t0+28) clipped to [tlo, thi] (the decode
 // path's deferred batches, split across the waves of a step).  Same
-// arithmetic per token as score_chunk: layer 1 on v_mfma_f32_32x32x16_bf16
+// arithmetic per token as score_pass: layer 1 on v_mfma_f32_32x32x16_bf16
 // over the 32 rows t0-2 .. t0+29, with W1's bf16 operands built from the fp32
 // weights; a token's score does not depend on how tokens are grouped.
 //   Ya       LDS of kWaveScoreBytesA: layer-1 taps 0 and 1 [32 rows][64], wave-private
 //   Yb       LDS of kWaveScoreBytesB: layer-1 tap 2 [32 rows][32], wave-private
 //   w1g      fp32 W1 of this head [hidden][2D][3]; w2g [hidden][3]
-constexpr int kWaveScoreTile = 28;
+constexpr int kWaveScoreTile = kPassTokens;
 constexpr int kWaveScoreBytesA = 32 * 64 * 4;
 constexpr int kWaveScoreBytesB = 32 * 32 * 4;
 
