@@ -30,6 +30,12 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+// Prompts of up to kSelLdsT tokens keep the whole per-(b, g) scratch (sort
+// buffers, snapshot bitmaps and their prefix counts: 128 KB) in LDS, which
+// turns every phase's global round trips into LDS ones; longer prompts use the
+// workspace.
+constexpr int kSelLdsT = 4096;
+constexpr int kSelLdsWords = 4 * kSelLdsT + 2 * (kSelLdsT / 64) * (kSelLdsT / 32);
 
 __device__ __forceinline__ unsigned long long lanemask_lt(int lane) {
     return lane == 0 ? 0ull : ((~0ull) >> (64 - lane));
@@ -59,7 +65,7 @@ __device__ __forceinline__ int block_excl_scan(int x, int* wsum, int* total) {
     return woff + incl - x;
 }
 
-template <int ELEMS>
+template <int ELEMS, bool LDS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int T, int Hkv, int s, int w, int C, int rbs, int nsnap_max, long scratch_words,
     const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
@@ -72,6 +78,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ int dbase[256];
     __shared__ int Msnap[1024];
     __shared__ int skip;
+    __shared__ __align__(16) uint32_t lsc[LDS ? kSelLdsWords : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -80,7 +87,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* r = scores + long(bg) * T;
     int32_t* rk = rank_out + long(bg) * T;
     int32_t* th = thr_out + long(bg) * T;
-    uint32_t* sc = scratch + long(bg) * scratch_words;
+    uint32_t* sc;
+    if constexpr (LDS) sc = lsc;
+    else sc = scratch + long(bg) * scratch_words;
     const long Tp = (long(T) + 63) & ~63L;           // 256-byte aligned array stride
     uint32_t* cidx = sc;
     uint32_t* ckey = sc + Tp;
@@ -331,14 +340,19 @@ hipError_t launch_select(const Shape& sh, int64_t T, const int32_t* seq_lens, co
     const int nsnap_max = int(select_nsnap_max(T));
     const long words = long(select_scratch_words(T));
     dim3 grid(unsigned(sh.B * sh.Hkv));
-    if (T <= 4 * kSelThreads) {
-        hipLaunchKernelGGL(select_kernel<4>, grid, dim3(kSelThreads), 0, st, int(T), sh.Hkv,
-                           sh.s, sh.w, sh.C, rbs, nsnap_max, words, seq_lens, scores, rank, thr,
-                           ncand, scratch);
+    if (T <= kSelLdsT && words <= kSelLdsWords) {
+        static_assert(kSelLdsT <= 4 * kSelThreads, "four sort elements per thread");
+        hipLaunchKernelGGL((select_kernel<4, true>), grid, dim3(kSelThreads), 0, st, int(T),
+                           sh.Hkv, sh.s, sh.w, sh.C, rbs, nsnap_max, words, seq_lens, scores,
+                           rank, thr, ncand, scratch);
+    } else if (T <= 4 * kSelThreads) {
+        hipLaunchKernelGGL((select_kernel<4, false>), grid, dim3(kSelThreads), 0, st, int(T),
+                           sh.Hkv, sh.s, sh.w, sh.C, rbs, nsnap_max, words, seq_lens, scores,
+                           rank, thr, ncand, scratch);
     } else {
-        hipLaunchKernelGGL(select_kernel<32>, grid, dim3(kSelThreads), 0, st, int(T), sh.Hkv,
-                           sh.s, sh.w, sh.C, rbs, nsnap_max, words, seq_lens, scores, rank, thr,
-                           ncand, scratch);
+        hipLaunchKernelGGL((select_kernel<32, false>), grid, dim3(kSelThreads), 0, st, int(T),
+                           sh.Hkv, sh.s, sh.w, sh.C, rbs, nsnap_max, words, seq_lens, scores,
+                           rank, thr, ncand, scratch);
     }
     return hipGetLastError();
 }
