@@ -46,6 +46,17 @@ MALL_BYTES = 256 * 2**20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+# A spin kernel queued ahead of a timed region's first event lets the host
+# enqueue every launch of the region while the GPU waits, so the events time the
+# GPU's work, not the host's launch latency after an idle queue.
+GATE_CYCLES = 400_000          # about 170 us of the GPU clock counter
+
+
+def gate():
+    import torch
+    torch.cuda._sleep(GATE_CYCLES)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,6 +228,7 @@ def _graph_us_per_step(layer, caches, qs, ks, vs, cnn, ws, reps=3):
     best = float("inf")
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gate()
         e0.record()
         g.replay()
         e1.record()
@@ -250,6 +262,7 @@ def comparators(inp, wl, T, dev, ndec=64):
         times = []
         for _ in range(5):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gate()
             e0.record()
             layer.prefill_attend(qp, kp, vp, ws, out)
             e1.record()
@@ -290,6 +303,7 @@ def linear_layer(dev, B=32, T=4096, H=16, D=128, ndec=64):
     times = []
     for _ in range(6):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gate()
         e0.record()
         layer.prefill(qp, kp, vp, ap, state_out=state, out=out)
         e1.record()
@@ -313,6 +327,7 @@ def linear_layer(dev, B=32, T=4096, H=16, D=128, ndec=64):
             layer.decode_step(dq[t], dk[t], dv[t], da[t], state, dout)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gate()
     e0.record()
     g.replay()
     e1.record()
@@ -377,6 +392,7 @@ def main():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
     def prefill_staged():
+        gate()
         ev[0].record(stream)
         layer.prefill_score(kp, vp, cnn, ws)
         ev[1].record(stream)
@@ -529,6 +545,7 @@ def main():
         for _ in range(6):
             c = cache0.clone()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gate()
             e0.record(stream)
             layer.prefill_chunk(qc, kc, vc, cnn, c, cws, cout)
             e1.record(stream)
