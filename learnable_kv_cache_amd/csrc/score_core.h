@@ -7,8 +7,8 @@
 // token is computable once its receptive field (tokens j-2 .. j+2 for two
 // kernel-3 layers) is present.
 //
-// score_pass: one wave of a prefill workgroup scores 28 tokens from A
-// fragments it already holds, with W1 staged once per workgroup in LDS.
+// score_pass: one wave of a prefill workgroup scores 28 tokens, loading its
+// 32 rows' k and v itself, with W1 staged once per workgroup in LDS.
 // score_wave: one wave scores 28 tokens (decode), W1 read from global memory.
 // Layer 1 is written as Y_tap = W1[:, :, tap] . x per token
 // (v_mfma_f32_32x32x16_bf16, 32 tokens x 96 outputs per wave), then
