@@ -20,8 +20,10 @@
  *   - scores and retention are per KV head (shared by the query heads of a
  *     GQA group, head h uses KV head h / (Hq/Hkv));
  *   - CNN per KV head: conv1d(2D -> hidden, kernel 3, zero pad 1) over
- *     concat(k, v) channels (keys first), exact GELU, conv1d(hidden -> 1,
- *     kernel 3, zero pad 1), sigmoid; tap t reads offset t-1;
+ *     concat(k, v) channels (keys first), GELU (erf evaluated by Abramowitz
+ *     and Stegun's formula 7.1.26, absolute error at most 1.5e-7),
+ *     conv1d(hidden -> 1, kernel 3, zero pad 1), sigmoid; tap t reads
+ *     offset t-1;
  *   - keep rule: a token j >= s is a candidate iff r_j > 0.5 (fp32); at most
  *     C are retained; on overflow the C best by (score descending, index
  *     ascending) stay; decisions are causal (query i sees the set built from
