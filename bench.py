@@ -391,6 +391,11 @@ def main():
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
+    # The cache build needs only select's outputs and k/v, and writes only the
+    # cache: it runs on a second stream beside the attention, which leaves LDS,
+    # registers and HBM bandwidth to spare (the ABI allows this pairing).
+    side_stream = torch.cuda.Stream()
+
     def prefill_staged():
         gate()
         ev[0].record(stream)
@@ -398,9 +403,12 @@ def main():
         ev[1].record(stream)
         layer.prefill_select(T, ws)
         ev[2].record(stream)
+        side_stream.wait_event(ev[2])
+        with torch.cuda.stream(side_stream):
+            layer.prefill_build_cache(kp, vp, ws, cache0)
         layer.prefill_attend(qp, kp, vp, ws, out)
         ev[3].record(stream)
-        layer.prefill_build_cache(kp, vp, ws, cache0)
+        stream.wait_stream(side_stream)
         ev[4].record(stream)
 
     prefill_staged()
@@ -486,7 +494,9 @@ def main():
                   "frac": kv_bytes / (score_ms * 1e-3) / PEAK_HBM_BPS},
         "select": {"ms": float(np.median(stage_ms["select"]))},
         "attend": {"ms": att_ms, "frac_mfma": achieved / PEAK_BF16_FLOPS},
-        "build_cache": {"ms": float(np.median(stage_ms["build_cache"]))},
+        # runs beside attend on a second stream: ms is the part left after attend ends
+        "build_cache": {"ms": float(np.median(stage_ms["build_cache"])),
+                        "beside_attend": True},
     }
     result = {
         "metric": METRIC,

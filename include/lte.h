@@ -226,7 +226,11 @@ int lte_prefill_chunk(const lte_config* cfg, int64_t n,
                       size_t workspace_bytes, uint16_t* out, void* stream);
 
 /* The four stages lte_prefill runs, in order, exposed for timing and tests.
- * Each reads and writes the workspace views described above. */
+ * Each reads and writes the workspace views described above.  Once
+ * lte_prefill_select has completed, lte_prefill_attend and
+ * lte_prefill_build_cache only read the workspace (scores, rank, thr), k and v,
+ * and write disjoint outputs (out; cache), so a caller may run them
+ * concurrently on two streams. */
 int lte_prefill_score(const lte_config* cfg, int64_t T, const uint16_t* k, const uint16_t* v,
                       const lte_cnn* cnn, void* workspace, size_t workspace_bytes, void* stream);
 int lte_prefill_select(const lte_config* cfg, int64_t T, const float* score_override,

@@ -143,6 +143,43 @@ def test_repeat_runs_are_bitwise_identical():
         assert np.array_equal(va[n], vb[n]), n
 
 
+def test_attend_beside_cache_build_matches_serial_prefill():
+    """After select, attend and the cache build share only read-only inputs: run on two
+    streams at once they give the serial prefill's output and cache bit for bit."""
+    inp = synth.workload_inputs(1)
+    wl = inp["workload"]
+    T = inp["T"]
+    q, k, v = (_dev(x) for x in (inp["q"], inp["k"], inp["v"]))
+    layer = lte.Layer(lte.Config(wl.B, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window, wl.capacity))
+    cnn = lte.CNN(inp["cnn"])
+    ws = layer.alloc_workspace(T)
+
+    def zeroed_cache():      # unused slots compare equal too
+        c = torch.zeros(layer.cache_bytes(), dtype=torch.uint8, device="cuda")
+        layer.cache_init(c)
+        return c
+
+    cache_a = zeroed_cache()
+    out_a = layer.prefill(q, k, v, cnn=cnn, cache=cache_a, workspace=ws)
+    torch.cuda.synchronize()
+    out_b = torch.empty_like(out_a)
+    cache_b = zeroed_cache()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    layer.prefill_score(k, v, cnn, ws)
+    layer.prefill_select(T, ws)
+    done = torch.cuda.Event()
+    done.record(main)
+    side.wait_event(done)
+    with torch.cuda.stream(side):
+        layer.prefill_build_cache(k, v, ws, cache_b)
+    layer.prefill_attend(q, k, v, ws, out_b)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(cache_a, cache_b)
+
+
 def _sample_rows(T, w, n=48, seed=0):
     rng = np.random.default_rng(seed)
     fixed = [0, 1, w - 1, w, w + 1, T - 1]
