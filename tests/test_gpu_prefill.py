@@ -113,6 +113,28 @@ def test_explicit_scores_exact_sets(shape):
     _check_rows(q, k, v, s, w, ends_g, out, list(range(T)), pairs)
 
 
+def _random_shape(seed):
+    """A small configuration drawn from a seed: every GQA group size and head size the
+    kernels instantiate, sink, window and capacity down to their edges, ragged T."""
+    rng = np.random.default_rng(1000 + seed)
+    G = [1, 2, 4, 8, 16][seed % 5]
+    Hkv = int(rng.choice([1, 2] if G >= 8 else [1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    s = int(rng.integers(0, 9))
+    w = int(rng.integers(5, 97))
+    C = 0 if rng.random() < 0.25 else int(rng.integers(1, 65))
+    T = int(rng.integers(1, 401))
+    B = int(rng.integers(1, 4))
+    levels = int(rng.choice([0, 2, 3, 5]))
+    return (B, T, G * Hkv, Hkv, D, s, w, C, levels)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_exact_sets(seed):
+    """Seeded random shapes through the same checks as the hand-picked ones."""
+    test_explicit_scores_exact_sets(_random_shape(seed))
+
+
 def test_all_kept_is_full_causal_and_none_kept_is_swa():
     """C >= T with every token kept equals full causal attention; retention 0 equals sink+SWA."""
     B, T, Hq, Hkv, D, s, w = 1, 160, 4, 2, 64, 2, 16
