@@ -137,6 +137,25 @@ def test_decode_full_size():
                       every=7)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shape_decode(seed):
+    """Seeded random decode configurations: group size, head size, sink, window,
+    capacity (overflowing or not), prompt length and step count."""
+    rng = np.random.default_rng(2000 + seed)
+    G = [1, 2, 4, 8, 16, 4][seed]
+    Hkv = int(rng.choice([1, 2]))
+    D = int(rng.choice([64, 128]))
+    s = int(rng.integers(0, 6))
+    w = int(rng.integers(5, 40))
+    C = int(rng.integers(1, 24))
+    T = int(rng.integers(1, 90))
+    n = int(rng.integers(20, 70))
+    b2 = float(rng.choice([0.0, 0.05, 0.5]))
+    B = int(rng.integers(1, 3))
+    q, k, v, cnn = synth.random_case(500 + seed, B, T + n, G * Hkv, Hkv, D, b2=b2)
+    run_decode_parity(B, T, n, G * Hkv, Hkv, D, s, w, C, q, k, v, cnn)
+
+
 @pytest.mark.parametrize("rho", [0.05, 0.2, 0.5])
 def test_long_context_decode(rho):
     """B4, 32768-token prompt, Hq32 Hkv8 D128 s4 w1024 C2048, 256 decode steps, with b2 set
