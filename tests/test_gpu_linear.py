@@ -65,6 +65,23 @@ def test_linear_prefill(T, D):
     _check_state(S, ref_S, "state")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_linear_random_shapes(seed):
+    """Seeded random batch, length, head count and size, decay strength, an initial
+    state or not, and a reset or not."""
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 400))
+    H = int(rng.integers(1, 5))
+    D = int(rng.choice([64, 128]))
+    gate = float(rng.choice([1.0, 4.0, 8.0]))
+    resets = (int(rng.integers(0, T)),) if rng.random() < 0.5 else ()
+    o, S, ref_o, ref_S = _run(B, T, H, D, seed=4000 + seed, state_in=bool(rng.random() < 0.5),
+                              resets=resets, gate_mean=gate)
+    _check(o, ref_o, "out")
+    _check_state(S, ref_S, "state")
+
+
 def test_linear_prefill_state_in_and_resets():
     """A nonzero initial state, and resets (a = 0) inside a chunk and on a chunk edge."""
     o, S, ref_o, ref_S = _run(2, 300, 4, 128, seed=7, state_in=True, resets=(37, 128, 131))
