@@ -257,6 +257,36 @@ def test_chunk_no_sink_or_no_segment(s, C):
     st.chunk(25)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_chunk_random_streams(seed):
+    """Seeded random streams: ragged prefill lengths, then four operations, each a chunk
+    or a run of decode steps, over random group size, head size, sink, window and
+    capacity."""
+    rng = np.random.default_rng(5000 + seed)
+    G = [1, 2, 4, 8][seed]
+    Hkv = int(rng.choice([1, 2]))
+    D = int(rng.choice([64, 128]))
+    s = int(rng.integers(0, 5))
+    w = int(rng.integers(5, 32))
+    C = int(rng.integers(0, 20))
+    B = int(rng.integers(1, 3))
+    lens = [int(rng.integers(1, 60)) for _ in range(B)]
+    ops, total = [], max(lens)
+    for _ in range(4):
+        if rng.random() < 0.5:
+            n = int(rng.integers(1, 80))
+            ops.append(("chunk", n))
+        else:
+            n = int(rng.integers(1, 30))
+            ops.append(("decode", n))
+        total += n
+    st = Stream(B, G * Hkv, Hkv, D, s, w, C, total + 1, seed=6000 + seed,
+                b2=float(rng.choice([0.02, 0.3])))
+    st.prefill(lens)
+    for op, n in ops:
+        getattr(st, op)(n)
+
+
 def test_long_chunk():
     """A chunk of 300 tokens, far longer than w + C: most of it leaves the window inside the
     call and the segment overflows repeatedly (G1, D64)."""
