@@ -174,9 +174,13 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
         }
     };
     auto stash = [&]() {
+        // the LDS offsets are recomputed here on every call: hoisted out of the chunk
+        // loop they were spilled, and their reloads serialised the stores
+        int tx = tid;
+        asm volatile("" : "+v"(tx));
 #pragma unroll
         for (int u = 0; u < LPT; ++u) {
-            const int x = tid + u * NT;
+            const int x = tx + u * NT;
             const int r = x / CPR;
             const int c = x % CPR;
             Qs[r * CPR + (c ^ rswz<D>(r))] = pq[u];
