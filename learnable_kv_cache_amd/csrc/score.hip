@@ -68,25 +68,31 @@ __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_e
     const int c_end = min(min(nchunk, (part + 1) * per), (Tb + kChunkTokens - 1) / kChunkTokens);
     if (c_begin >= c_end) return;
 
+    const long row_stride = long(Hkv) * D;
+    const uint16_t* kb = k + (long(b) * T * Hkv + g) * D;
+    const uint16_t* vb = v + (long(b) * T * Hkv + g) * D;
+    // this lane's row of the first pass: its first operand half loads while W1 is staged
+    int tok = c_begin * kChunkTokens + wave * kPassTokens - 2 + (lane & 31);
+    bf16x8 a0[ScoreSmem<D>::KK / 2];
+    score_load_half<D>(a0, kb + long(tok) * row_stride, vb + long(tok) * row_stride,
+                       tok >= 0 && tok < Tb, 0);
+
     const bf16x8* wsrc = w1p + long(g) * NW;
     for (int x = tid; x < NW; x += 64 * kScoreWaves) wl[x] = wsrc[x];
     for (int x = tid; x < kHidden * 3; x += 64 * kScoreWaves) w2s[x] = w2[g * kHidden * 3 + x];
     const float b1o = b1[g * kHidden + (lane & 31)];
     const float b2g = b2[g];
 
-    const long row_stride = long(Hkv) * D;
-    const uint16_t* kb = k + (long(b) * T * Hkv + g) * D;
-    const uint16_t* vb = v + (long(b) * T * Hkv + g) * D;
     float* out = scores + long(bg) * T;
     __syncthreads();                                         // W1 and W2 staged
     float* my_act = act[wave];
-    for (int c = c_begin; c < c_end; ++c) {
+    for (int c = c_begin; c < c_end; ++c, tok += kChunkTokens) {
         const int t0 = c * kChunkTokens + wave * kPassTokens;
-        const int tok = t0 - 2 + (lane & 31);                // this lane's row
-        const bool ok = tok >= 0 && tok < Tb;
+        const int ntok = tok + kChunkTokens;                 // the same row of the next pass
         score_pass<D>(
-            wl, w2s, b1o, b2g, kb + long(tok) * row_stride, vb + long(tok) * row_stride, ok,
-            my_act, t0, 0, Tb - 1,
+            wl, w2s, b1o, b2g, a0, kb + long(tok) * row_stride, vb + long(tok) * row_stride,
+            tok >= 0 && tok < Tb, kb + long(ntok) * row_stride, vb + long(ntok) * row_stride,
+            c + 1 < c_end && ntok < Tb, my_act, t0, 0, Tb - 1,
             [&](int x) { return x < 0 || x >= Tb; },
             [&](int t, float r) { if (t >= lo) out[t] = r; });
     }

@@ -69,12 +69,31 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// Half hf of a lane's layer-1 A operands: k-steps hf*KK/2 .. +KK/2, i.e.
+// channels 16 kk + 8 (lane/32) .. +8 of concat(k, v) of the row at kp, vp
+// (zeros where !ok).
+template <int D>
+__device__ __forceinline__ void score_load_half(bf16x8 (&a)[ScoreSmem<D>::KK / 2],
+                                                const uint16_t* kp, const uint16_t* vp, bool ok,
+                                                int hf) {
+    constexpr int KH = ScoreSmem<D>::KK / 2;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < KH; ++q) {
+        const int ch = (hf * KH + q) * 16 + (lane >> 5) * 8;
+        a[q] = ok ? *reinterpret_cast<const bf16x8*>((ch < D) ? (kp + ch) : (vp + (ch - D)))
+                  : bf16x8{};
+    }
+}
+
 // Scores tokens [t0, t0+28) clipped to [tlo, thi] and hands each to store(t, r).
 //   wl       this head's packed W1 in LDS
 //   w2s      this head's W2 [32][3] in LDS
 //   b1o      b1 of output column lane % 32
-//   kp, vp   k and v row of this lane's token (row lane % 32: token t0 - 2 + lane % 32), if ok;
-//            the A operand of k-step kk is channels 16 kk + 8 (lane/32) .. +8 of concat(k, v)
+//   a0       half 0 of this pass's A operands, loaded by the caller (score_load_half);
+//            on return it holds half 0 of the next pass's, from nkp, nvp (zeros where !nok),
+//            whose loads run under this pass's activation and output-layer work
+//   kp, vp   k and v row of this lane's token (row lane % 32: token t0 - 2 + lane % 32), if ok
 //   act      wave-private LDS tile [kActRows][kActPitch]: hidden activations of rows 1 .. 30
 //   a_zero(x) -> true where layer 2 sees zero padding (outside the sequence)
 // The accumulator element e of lane l holds row 8 (e/4) + 4 (l/32) + e%4 and
@@ -82,8 +101,10 @@ __device__ __forceinline__ float other_half(float x) {
 // across groups of 4 rows, where they sit in lane l ^ 32.
 template <int D, class AZero, class Store>
 __device__ __forceinline__ void score_pass(const bf16x8* wl, const float* w2s, float b1o,
-                                           float b2g, const uint16_t* kp, const uint16_t* vp,
-                                           bool ok, float* act, int t0, int tlo, int thi,
+                                           float b2g, bf16x8 (&a0)[ScoreSmem<D>::KK / 2],
+                                           const uint16_t* kp, const uint16_t* vp, bool ok,
+                                           const uint16_t* nkp, const uint16_t* nvp, bool nok,
+                                           float* act, int t0, int tlo, int thi,
                                            AZero a_zero, Store store) {
     constexpr int KK = ScoreSmem<D>::KK;
     constexpr int KH = KK / 2;                       // k-steps per operand half
@@ -95,24 +116,29 @@ __device__ __forceinline__ void score_pass(const bf16x8* wl, const float* w2s, f
     // the A operands in two halves of the channels, to keep registers for
     // four waves per SIMD
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 afrag[KH];
+    for (int q = 0; q < KH; ++q) {
 #pragma unroll
-        for (int q = 0; q < KH; ++q) {
-            const int ch = (hf * KH + q) * 16 + (lane >> 5) * 8;
-            afrag[q] = ok ? *reinterpret_cast<const bf16x8*>((ch < D) ? (kp + ch) : (vp + (ch - D)))
-                          : bf16x8{};
+        for (int tp = 0; tp < 3; ++tp) {
+            const bf16x8 bfrag = wl[(tp * KK + q) * 64 + lane];
+            acc[tp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], bfrag, acc[tp], 0, 0, 0);
         }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        bf16x8 a1[KH];
+        score_load_half<D>(a1, kp, vp, ok, 1);
 #pragma unroll
         for (int q = 0; q < KH; ++q) {
 #pragma unroll
             for (int tp = 0; tp < 3; ++tp) {
-                const bf16x8 bfrag = wl[(tp * KK + hf * KH + q) * 64 + lane];
-                acc[tp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[q], bfrag, acc[tp], 0, 0, 0);
+                const bf16x8 bfrag = wl[(tp * KK + KH + q) * 64 + lane];
+                acc[tp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], bfrag, acc[tp], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    score_load_half<D>(a0, nkp, nvp, nok, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // tap 0 of row-1 and tap 2 of row+1 where they sit in the other lane half
     float p0[4], p2[4];
 #pragma unroll
