@@ -41,6 +41,17 @@ __device__ __forceinline__ unsigned long long lanemask_lt(int lane) {
     return lane == 0 ? 0ull : ((~0ull) >> (64 - lane));
 }
 
+// Lanes of this wave that are valid and hold the digit d (8 bits) of this lane.
+__device__ __forceinline__ unsigned long long same_digit(int d, bool valid) {
+    unsigned long long mask = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const unsigned long long bb = __ballot((d >> bit) & 1);
+        mask &= ((d >> bit) & 1) ? bb : ~bb;
+    }
+    return mask;
+}
+
 // Block-wide exclusive scan of one int per thread (1024 threads).
 __device__ __forceinline__ int block_excl_scan(int x, int* wsum, int* total) {
     const int lane = threadIdx.x & 63;
@@ -77,13 +88,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ int wcnt[kSelWaves][256];
     __shared__ int dbase[256];
     __shared__ int Msnap[1024];
-    __shared__ int skip;
+    __shared__ int skipf[4];                        // per radix pass: every key has one digit
     __shared__ __align__(16) uint32_t lsc[LDS ? kSelLdsWords : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int bg = blockIdx.x;
+    if (tid < 4) skipf[tid] = 0;                   // read after the barriers below
     const float* r = scores + long(bg) * T;
     int32_t* rk = rank_out + long(bg) * T;
     int32_t* th = thr_out + long(bg) * T;
@@ -132,30 +144,47 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
 
     // ---- 2. stable LSD radix sort, 8 bits per pass ---------------------------
+    // Wave w holds sequence positions [w*ELEMS*64, (w+1)*ELEMS*64), element e of
+    // lane l at position (w*ELEMS + e)*64 + l.  A pass ranks each wave's
+    // elements against its own digit counters, 64 at a time in position order
+    // (no block barrier between groups), then one scan over (digit, wave)
+    // turns the counters into each (wave, digit)'s first output position and
+    // the same walk places the elements: the order within a digit is kept.
     uint32_t key[ELEMS], idx[ELEMS];
+    const int wbase = wave * ELEMS * 64;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < ELEMS; ++e) {
-        int p = e * kSelThreads + tid;
+        const int p = wbase + e * 64 + lane;
         key[e] = p < n ? ckey[p] : 0u;
         idx[e] = p < n ? cidx[p] : 0u;
     }
     bool in_tmp = false;                                // where the sorted data lives
     for (int shift = 0; shift < 32; shift += 8) {
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
+        int* wc = wcnt[wave];
+        for (int x = lane; x < 256; x += 64) wc[x] = 0;
 #pragma unroll
         for (int e = 0; e < ELEMS; ++e) {
-            int p = e * kSelThreads + tid;
-            if (p < n) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
+            if (wbase + e * 64 >= n) break;             // uniform across the wave
+            const bool valid = wbase + e * 64 + lane < n;
+            const int d = int((key[e] >> shift) & 255);
+            const unsigned long long mask = same_digit(d, valid);
+            const int before = valid ? wc[d] : 0;       // this digit in earlier groups
+            if (valid && __popcll(mask & lanemask_lt(lane)) == 0) wc[d] = before + __popcll(mask);
         }
         __syncthreads();
-        // a pass in which every key has the same digit leaves the order as is
-        // (thread 0's first element exists: n > C >= 1)
-        if (tid == 0) skip = (hist[(key[0] >> shift) & 255] == n) ? 1 : 0;
+        // digit totals; a pass in which every key has the same digit leaves the
+        // order as is
+        if (tid < 256) {
+            int tot = 0;
+#pragma unroll
+            for (int q = 0; q < kSelWaves; ++q) tot += wcnt[q][tid];
+            hist[tid] = tot;
+            if (tot == n) skipf[shift >> 3] = 1;
+        }
         __syncthreads();
-        if (skip) continue;
-        // exclusive scan of the 256-bin histogram (wave 0, 4 bins per lane)
+        if (skipf[shift >> 3]) continue;
+        // exclusive scan of the 256 digit totals (wave 0, 4 digits per lane)
         if (wave == 0) {
             int h0 = hist[lane * 4 + 0], h1 = hist[lane * 4 + 1];
             int h2 = hist[lane * 4 + 2], h3 = hist[lane * 4 + 3];
@@ -172,59 +201,52 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             dbase[lane * 4 + 2] = ex + h0 + h1;
             dbase[lane * 4 + 3] = ex + h0 + h1 + h2;
         }
+        __syncthreads();
+        // first output position of (wave q, digit): digit base plus the digit's
+        // count in the waves before q
+        if (tid < 256) {
+            int run = dbase[tid];
+#pragma unroll
+            for (int q = 0; q < kSelWaves; ++q) {
+                const int c = wcnt[q][tid];
+                wcnt[q][tid] = run;
+                run += c;
+            }
+        }
+        __syncthreads();
         uint32_t* okey = in_tmp ? ckey : tkey;
         uint32_t* oidx = in_tmp ? cidx : tidx;
 #pragma unroll
         for (int e = 0; e < ELEMS; ++e) {
-            const int p = e * kSelThreads + tid;
-            if (e * kSelThreads >= n) break;            // uniform across the block
-            for (int x = tid; x < kSelWaves * 256; x += kSelThreads) (&wcnt[0][0])[x] = 0;
-            __syncthreads();
-            const bool valid = p < n;
+            if (wbase + e * 64 >= n) break;
+            const bool valid = wbase + e * 64 + lane < n;
             const int d = int((key[e] >> shift) & 255);
-            unsigned long long mask = __ballot(valid);
-#pragma unroll
-            for (int bit = 0; bit < 8; ++bit) {
-                unsigned long long bb = __ballot((d >> bit) & 1);
-                mask &= ((d >> bit) & 1) ? bb : ~bb;
-            }
+            const unsigned long long mask = same_digit(d, valid);
             const int lrank = __popcll(mask & lanemask_lt(lane));
-            if (valid && lrank == 0) wcnt[wave][d] = __popcll(mask);
-            __syncthreads();
-            if (tid < 256) {
-                int run = dbase[tid];
-#pragma unroll
-                for (int q = 0; q < kSelWaves; ++q) {
-                    int c = wcnt[q][tid];
-                    wcnt[q][tid] = run;
-                    run += c;
-                }
-                dbase[tid] = run;
-            }
-            __syncthreads();
+            const int at = valid ? wc[d] : 0;           // next free position of the digit
             if (valid) {
-                const int dst = wcnt[wave][d] + lrank;
-                okey[dst] = key[e];
-                oidx[dst] = idx[e];
+                okey[at + lrank] = key[e];
+                oidx[at + lrank] = idx[e];
+                if (lrank == 0) wc[d] = at + __popcll(mask);
             }
-            __syncthreads();
         }
         in_tmp = !in_tmp;
         __threadfence_block();
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < ELEMS; ++e) {
-            int p = e * kSelThreads + tid;
+            const int p = wbase + e * 64 + lane;
             key[e] = p < n ? okey[p] : 0u;
             idx[e] = p < n ? oidx[p] : 0u;
         }
         __syncthreads();
     }
-    // key/idx registers now hold the sorted order: element p = e*1024 + tid.
+    // key/idx registers now hold the sorted order: element e of this lane is at
+    // position wbase + e*64 + lane.
     const uint32_t* sidx = in_tmp ? tidx : cidx;
 #pragma unroll
     for (int e = 0; e < ELEMS; ++e) {
-        int p = e * kSelThreads + tid;
+        int p = wbase + e * 64 + lane;
         if (p < n) rk[idx[e]] = p;
     }
 
@@ -235,7 +257,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < ELEMS; ++e) {
-        int p = e * kSelThreads + tid;
+        int p = wbase + e * 64 + lane;
         if (p < n) {
             uint32_t j = idx[e];
             atomicOr(&bm[long(p / rbs) * W + (j >> 5)], 1u << (j & 31));
