@@ -115,12 +115,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int Tb = seq_len_of(seq_lens, bg / Hkv, T);    // this sequence's length
     const int last_leaving = Tb - 1 - w;             // last token that leaves the window
     int n = 0;
+    float r_next = (tid < T) ? r[tid] : 0.0f;       // scores read one group ahead
     for (int base = 0; base < T; base += kSelThreads) {
         const int j = base + tid;
+        const float rj = r_next;
+        if (j + kSelThreads < T) r_next = r[j + kSelThreads];
         bool cand = false;
-        float rj = 0.0f;
         if (j < T) {
-            rj = r[j];
             cand = (j >= s) && (j <= last_leaving) && (rj > 0.5f);
             rk[j] = kNotCand;
         }
@@ -342,10 +343,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 const uint32_t e4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
+                    // branch-free: need keeps counting down past zero, so it equals
+                    // zero right after exactly one hit, the need-th
                     const int p = c + 4 * q + u;
-                    if (need > 0 && p < p1 && e4[u] <= uint32_t(m)) {
-                        if (--need == 0) res = p;
-                    }
+                    const int hit = (p < p1 && e4[u] <= uint32_t(m)) ? 1 : 0;
+                    need -= hit;
+                    res = (hit != 0 && need == 0) ? p : res;
                 }
             }
         }
