@@ -113,6 +113,28 @@ def test_explicit_scores_exact_sets(shape):
     _check_rows(q, k, v, s, w, ends_g, out, list(range(T)), pairs)
 
 
+@pytest.mark.parametrize("shape", [
+    # B, T, Hq, Hkv, D, s, w, C, levels
+    (1, 4096, 4, 2, 64, 4, 64, 300, 3),     # every wave of the selection holds candidates
+    (1, 8192, 4, 1, 64, 4, 64, 700, 4),     # longer than the LDS-resident selection
+], ids=lambda s: "B{}T{}Hkv{}C{}levels{}".format(s[0], s[1], s[3], s[7], s[8]))
+def test_tied_scores_long_prompt_exact_sets(shape):
+    """Thousands of candidates on a few score levels: the top-C order among equal scores
+    (lower index first) decides most of the set, so the sort must be stable across the
+    whole candidate array; keep sets exact, sampled rows against the oracle."""
+    B, T, Hq, Hkv, D, s, w, C, levels = shape
+    q, k, v = synth.make_qkv(B, T, Hq, Hkv, D, seed=91 + T)
+    rng = np.random.default_rng(T + 5)
+    r = rng.choice(np.linspace(0.55, 0.95, levels), size=(B, Hkv, T)).astype(np.float32)
+    out, views, _, _ = run_prefill(B, T, Hq, Hkv, D, s, w, C, q, k, v, override=r)
+    ends_or = oracle.all_ends(r, s, w, C, T)
+    ends_g = _ends_all(views, w, T)
+    np.testing.assert_array_equal(normalize_ends(ends_g, w), normalize_ends(ends_or, w))
+    rows = sorted(set(rng.integers(0, T, 48).tolist()) | {0, w, T - 1})
+    pairs = [(b, g) for b in range(B) for g in range(Hkv)]
+    _check_rows(q, k, v, s, w, ends_g, out, rows, pairs)
+
+
 def _random_shape(seed):
     """A small configuration drawn from a seed: every GQA group size and head size the
     kernels instantiate, sink, window and capacity down to their edges, ragged T."""
