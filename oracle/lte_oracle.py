@@ -54,8 +54,8 @@ import numpy as np
 from scipy.special import erf
 
 __all__ = [
-    "cnn_logits", "cnn_scores", "retention_ends", "retained_set", "visible_indices",
-    "attention", "prefill", "LayerCache",
+    "cnn_logits", "cnn_scores", "retention_ends", "retained_set", "visible_set",
+    "visible_indices", "attention", "attention_on_set", "prefill", "LayerCache",
 ]
 
 
@@ -153,11 +153,16 @@ def retained_set(end: np.ndarray, w: int, i: int) -> np.ndarray:
     return np.nonzero((end >= 0) & (j + w <= i) & (i < end))[0]
 
 
-def visible_indices(i: int, s: int, w: int, end: np.ndarray) -> np.ndarray:
-    """V(i) = sink U window U R_i as sorted unique indices (reading R6)."""
+def visible_set(i: int, s: int, w: int, R) -> np.ndarray:
+    """V(i) = sink U window U R as sorted unique indices, for a retained set R (R6)."""
     sink = np.arange(0, min(s, i + 1))
     window = np.arange(max(0, i - w + 1), i + 1)
-    return np.union1d(np.union1d(sink, window), retained_set(end, w, i))
+    return np.union1d(np.union1d(sink, window), np.asarray(list(R), np.int64))
+
+
+def visible_indices(i: int, s: int, w: int, end: np.ndarray) -> np.ndarray:
+    """V(i) = sink U window U R_i as sorted unique indices (reading R6)."""
+    return visible_set(i, s, w, retained_set(end, w, i))
 
 
 # --------------------------------------------------------------------------
@@ -182,18 +187,39 @@ def attention(q, k, v, s: int, w: int, ends: np.ndarray, dtype=np.float64,
     out = np.full((B, T, Hq, D), np.nan, dtype)
     rows = range(T) if rows is None else rows
     pairs = [(b, g) for b in range(B) for g in range(Hkv)] if pairs is None else pairs
-    scale = 1.0 / math.sqrt(D)
     for (b, g) in pairs:
         for i in rows:
             idx = visible_indices(int(i), s, w, ends[b, g])
-            K = k[b, idx, g, :].astype(dtype)
-            V = v[b, idx, g, :].astype(dtype)
-            Q = q[b, i, g * G:(g + 1) * G, :].astype(dtype)
-            logits = (Q @ K.T) * dtype(scale)                 # [G, |V(i)|]
-            m = logits.max(axis=1, keepdims=True)
-            p = np.exp(logits - m)
-            out[b, i, g * G:(g + 1) * G, :] = (p @ V) / p.sum(axis=1, keepdims=True)
+            out[b, i, g * G:(g + 1) * G, :] = _softmax_rows(q[b, i, g * G:(g + 1) * G, :],
+                                                           k[b, idx, g, :], v[b, idx, g, :],
+                                                           dtype)
     return out
+
+
+def _softmax_rows(Q, K, V, dtype) -> np.ndarray:
+    """softmax(Q K^T / sqrt(D)) V for the query rows Q [G, D] over the keys K, V [n, D]."""
+    Q = np.asarray(Q).astype(dtype)
+    K = np.asarray(K).astype(dtype)
+    V = np.asarray(V).astype(dtype)
+    logits = (Q @ K.T) * dtype(1.0 / math.sqrt(Q.shape[-1]))      # [G, n]
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
+def attention_on_set(q, k, v, s: int, w: int, b: int, i: int, g: int, R,
+                     dtype=np.float64) -> np.ndarray:
+    """o of query row i of KV head g in sequence b ([G, D]) when the retained set at
+    that step is R: the same softmax as ``attention`` over sink U window U R.
+
+    Used to check a keep set realised elsewhere (the GPU's), where several sets are
+    correct for tokens scored at a threshold; q [B, T, Hq, D], k, v [B, T, Hkv, D].
+    """
+    q = np.asarray(q)
+    G = q.shape[2] // np.asarray(k).shape[2]
+    idx = visible_set(int(i), s, w, R)
+    return _softmax_rows(q[b, i, g * G:(g + 1) * G, :], np.asarray(k)[b, idx, g, :],
+                         np.asarray(v)[b, idx, g, :], dtype)
 
 
 def all_ends(scores: np.ndarray, s: int, w: int, C: int, steps: int) -> np.ndarray:

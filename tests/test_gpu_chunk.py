@@ -21,7 +21,7 @@ import torch
 import oracle
 from learnable_kv_cache_amd import lte, synth
 from tests.parity import BAND, MAX_ABS, MEAN_ABS, NOT_CAND
-from tests.test_gpu_decode import SCORE_TOL, _attend_on_set
+from tests.test_gpu_decode import SCORE_TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -31,8 +31,11 @@ class Stream:
     through prefill, chunks and decode steps and is checked after each."""
 
     def __init__(self, B, Hq, Hkv, D, s, w, C, total=None, seed=None, b2=None, inputs=None,
-                 check_b=None, every=1):
+                 check_b=None, every=1, exact=False):
         self.B, self.Hq, self.Hkv, self.D, self.s, self.w, self.C = B, Hq, Hkv, D, s, w, C
+        # exact: scores tie exactly and lie far from every threshold, so no token is
+        # exempt and every set must equal the oracle's
+        self.exact = exact
         self.G = Hq // Hkv
         if inputs is None:
             inputs = synth.random_case(seed, B, total, Hq, Hkv, D, b2=b2)
@@ -111,11 +114,8 @@ class Stream:
                     for j in R ^ Ro:
                         rj = float(bg_scores[j])
                         ok = abs(rj - 0.5) <= BAND or (cut is not None and abs(rj - cut) <= BAND)
-                        assert ok, ("chunk set", b, g, i, j, rj, cut)
-                    vis = sorted(set(range(min(s, i + 1))) | set(range(max(0, i - w + 1), i + 1))
-                                 | R)
-                    ref = _attend_on_set(self.qn[bi, i, sl], self.kn[bi, :, g], self.vn[bi, :, g],
-                                         np.array(vis, np.int64), self.G)
+                        assert ok and not self.exact, ("chunk set", b, g, i, j, rj, cut)
+                    ref = oracle.attention_on_set(self.qn, self.kn, self.vn, s, w, bi, i, g, R)
                     errs.append(np.abs(o[b, qi, sl] - ref))
                 d = np.stack(errs)
                 assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, ("chunk out", b, g, d.max(),
@@ -138,10 +138,8 @@ class Stream:
                 for g in range(self.Hkv):
                     gset = set(ret_idx[b, g, :count[b, g]].tolist())
                     sl = slice(g * self.G, (g + 1) * self.G)
-                    vis = sorted(set(range(min(self.s, t + 1)))
-                                 | set(range(max(0, t - self.w + 1), t + 1)) | gset)
-                    ref = _attend_on_set(self.qn[bi, t, sl], self.kn[bi, :, g], self.vn[bi, :, g],
-                                         np.array(vis, np.int64), self.G)
+                    ref = oracle.attention_on_set(self.qn, self.kn, self.vn, self.s, self.w, bi,
+                                                  t, g, gset)
                     d = np.abs(og[b, sl] - ref)
                     assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, ("decode", t, b, g)
             self.pos = [p + 1 for p in self.pos]
@@ -152,6 +150,16 @@ class Stream:
         """fresh: after a prefill or chunk (no deferred scoring pending)."""
         s, w, C = self.s, self.w, self.C
         v = {nm: x.cpu().numpy() for nm, x in self.views.items() if nm not in ("k", "v")}
+        # the exported bookkeeping is the cache's own
+        ex = self.layer.cache_export(self.cache)
+        for nm in ("count", "pos"):
+            assert np.array_equal(ex[nm].numpy(), v[nm]), nm
+        for b in range(self.B):
+            for g in range(self.Hkv):
+                cnt = int(v["count"][b, g])
+                assert np.array_equal(ex["ret_idx"][b, g, :cnt].numpy(), v["ret_idx"][b, g, :cnt])
+                assert np.array_equal(ex["ret_score"][b, g, :cnt].numpy(),
+                                      v["ret_score"][b, g, :cnt])
         assert int(v["flags"].max()) == 0, "a token left the window unscored"
         kc = self.views["k"].float().cpu().numpy()
         for b in range(self.B):
@@ -178,7 +186,12 @@ class Stream:
                 for j in gset ^ oset:
                     rj = float(self.r_all[bi, g, j])
                     ok = abs(rj - 0.5) <= BAND or (cut is not None and abs(rj - cut) <= BAND)
-                    assert ok, ("cache set", T, b, g, j, rj, cut)
+                    assert ok and not self.exact, ("cache set", T, b, g, j, rj, cut)
+                # retained entries carry their tokens' scores
+                for x in range(cnt):
+                    j = int(v["ret_idx"][b, g, x])
+                    assert abs(float(v["ret_score"][b, g, x]) - float(self.r_all[bi, g, j])) <= \
+                        SCORE_TOL, (b, g, x, j)
                 # retained K rows hold their tokens' keys
                 for x in range(cnt):
                     j = int(v["ret_idx"][b, g, x])
@@ -294,3 +307,18 @@ def test_long_chunk():
     st.prefill([90])
     st.chunk(300)
     st.decode(5)
+
+
+@pytest.mark.parametrize("kind", ["flat", "level"])
+def test_chunk_exact_ties(kind):
+    """Scores that tie exactly (see tests/ties.py): after a prefill, chunks and decode steps
+    the chunk queries' retained sets and the cache's segment must equal the oracle's
+    exactly, ties resolved by the lower index (B2 Hq8 Hkv2 D128 s3 w24 C9, overflowing)."""
+    from tests import ties
+    make = ties.flat_case if kind == "flat" else ties.level_case
+    st = Stream(2, 8, 2, 128, 3, 24, 9, inputs=make(77, 2, 420, 8, 2, 128), exact=True)
+    st.prefill([150, 97])
+    st.chunk(60)
+    st.decode(31)
+    st.chunk(120)
+    st.decode(12)

@@ -268,3 +268,34 @@ def test_full_layer_prefill_full_size():
     pairs = [(0, 0), (9, 1), (17, 2), (31, 3)]
     _check_rows(inp["q"], inp["k"], inp["v"], wl.sink, wl.window, ends_g, out,
                 _sample_rows(T, wl.window, seed=3), pairs)
+
+
+@pytest.mark.parametrize("shape", [
+    # B, T, Hq, Hkv, D, s, w, C, levels
+    (2, 300, 8, 2, 64, 4, 40, 30, 3),
+    (1, 1000, 16, 4, 128, 4, 128, 64, 0),
+    (2, 50, 4, 1, 64, 2, 64, 8, 2),          # shorter than the window: nothing left it
+], ids=lambda s: "B{}T{}Hkv{}w{}C{}".format(s[0], s[1], s[3], s[6], s[7]))
+def test_export_after_explicit_score_prefill(shape):
+    """lte_cache_export after a prefill with given scores (Figure 3's cache layout): the
+    exported segment is exactly R_{T-1} of the oracle, each entry with its token's score,
+    count = |R_{T-1}|, pos = T."""
+    B, T, Hq, Hkv, D, s, w, C, levels = shape
+    q, k, v = synth.make_qkv(B, T, Hq, Hkv, D, seed=88 + T)
+    rng = np.random.default_rng(T + 9)
+    if levels:
+        r = rng.choice(np.linspace(0.3, 0.9, 5), size=(B, Hkv, T)).astype(np.float32)
+    else:
+        r = rng.uniform(0.2, 1.0, size=(B, Hkv, T)).astype(np.float32)
+    _, _, layer, cache = run_prefill(B, T, Hq, Hkv, D, s, w, C, q, k, v, override=r,
+                                     with_cache=True)
+    ex = layer.cache_export(cache)
+    ends_or = oracle.all_ends(r, s, w, C, T)
+    assert np.all(ex["pos"].numpy() == T)
+    for b in range(B):
+        for g in range(Hkv):
+            want = oracle.retained_set(ends_or[b, g], w, T - 1)
+            cnt = int(ex["count"][b, g])
+            idx = ex["ret_idx"][b, g, :cnt].numpy()
+            assert cnt == len(want) and sorted(idx.tolist()) == want.tolist(), (b, g)
+            assert np.array_equal(ex["ret_score"][b, g, :cnt].numpy(), r[b, g, idx])

@@ -16,7 +16,7 @@ import torch
 import oracle
 from learnable_kv_cache_amd import lte, synth
 from tests.parity import BAND, MAX_ABS, MEAN_ABS, gpu_ends, keep_set_mismatches, output_errors
-from tests.test_gpu_decode import SCORE_TOL, _attend_on_set
+from tests.test_gpu_decode import SCORE_TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -114,10 +114,7 @@ def test_ragged_prefill_then_decode():
                     rj = float(r_all[b, g, j])
                     ok = abs(rj - 0.5) <= BAND or (cut is not None and abs(rj - cut) <= BAND)
                     assert ok, (step, b, g, j, rj, cut)
-                vis = sorted(set(range(min(s, t + 1))) | set(range(max(0, t - w + 1), t + 1))
-                             | gset)
-                ref = _attend_on_set(qn[b, t, g * G:(g + 1) * G], kn[b, :, g], vn[b, :, g],
-                                     np.array(vis, np.int64), G)
+                ref = oracle.attention_on_set(qn, kn, vn, s, w, b, t, g, gset)
                 d = np.abs(og[b, g * G:(g + 1) * G] - ref)
                 assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, (step, b, g, d.max())
 

@@ -123,3 +123,38 @@ def test_zero_queries_spell_out_the_visible_set():
             bits = int(round(o[0, i, 0, 0] * n))
             assert bits == sum(1 << j for j in case["visible"][i]), i
             assert o[0, i, 1, 0] == o[0, i, 0, 0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_on_a_given_set(seed):
+    """attention_on_set (the oracle's softmax over sink U window U a given retained set)
+    equals the dense float64 brute force with that mask, for arbitrary sets, and equals
+    ``attention`` when the set is the oracle's own R_i."""
+    from oracle import attention_on_set, retained_set
+    rng = np.random.default_rng(500 + seed)
+    T, s, w, C = int(rng.integers(20, 80)), int(rng.integers(0, 4)), int(rng.integers(5, 12)), 6
+    G = [1, 2, 4][seed % 3]
+    Hkv, D, B = 2, 8, 2
+    q, k, v = _rand_qkv(rng, B, T, Hkv * G, Hkv, D)
+    scores = rng.uniform(0.3, 1.0, size=(B, Hkv, T)).astype(np.float32)
+    full = prefill(q, k, v, s, w, C, scores=scores)
+    for b in range(B):
+        for g in range(Hkv):
+            for i in rng.integers(0, T, 6).tolist():
+                R = retained_set(full["ends"][b, g], w, i)
+                np.testing.assert_array_equal(
+                    attention_on_set(q, k, v, s, w, b, i, g, R),
+                    full["o"][b, i, g * G:(g + 1) * G])
+                # an arbitrary set of earlier tokens, outside any keep rule
+                Rx = sorted(set(rng.integers(0, i + 1, 5).tolist()))
+                mask = np.zeros((T, T), bool)
+                mask[i, :min(s, i + 1)] = True
+                mask[i, max(0, i - w + 1):i + 1] = True
+                mask[i, Rx] = True
+                others = np.arange(T) != i                   # other rows: any valid mask
+                mask[others, others] = True
+                masks = np.broadcast_to(np.eye(T, dtype=bool), (B, Hkv, T, T)).copy()
+                masks[b, g] = mask
+                want = dense_attention(q, k, v, masks)[b, i, g * G:(g + 1) * G]
+                np.testing.assert_allclose(attention_on_set(q, k, v, s, w, b, i, g, Rx), want,
+                                           rtol=1e-10, atol=1e-12)

@@ -95,3 +95,30 @@ def test_zero_weights_give_the_bias():
                    np.zeros((2, hidden), np.float32), np.zeros((2, hidden, 3), np.float32),
                    np.zeros(2, np.float32))
     assert np.all(r == np.float32(0.5))
+
+
+def test_sigmoid_matches_library():
+    """Library pin of the score's last step: r = sigmoid(z) stored as fp32 equals torch's
+    float64 sigmoid rounded to fp32 (within one fp32 ulp where float64 rounding orders
+    differ), and scipy's expit; the orientation is fixed by sigmoid(2) > 1/2 > sigmoid(-2)."""
+    from scipy.special import expit
+
+    from oracle import sigmoid_to_f32
+    z = np.concatenate([np.linspace(-30.0, 30.0, 6001), [0.0, -0.0, 1e-8, -1e-8, 0.4, -0.4]])
+    ours = sigmoid_to_f32(z)
+    assert ours.dtype == np.float32
+    ref = torch.sigmoid(torch.as_tensor(z, dtype=torch.float64)).to(torch.float32).numpy()
+    ulps = np.abs(ours.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    assert (ulps == 0).mean() > 0.999
+    np.testing.assert_allclose(ours, expit(z), rtol=1e-7, atol=0)
+    assert np.all(np.diff(ours[:6001]) >= 0)                 # increasing in z
+    two = sigmoid_to_f32(np.array([2.0, 0.0, -2.0]))
+    assert two[0] > 0.5 and two[1] == np.float32(0.5) and two[2] < 0.5
+    np.testing.assert_allclose(two[0], 0.8807970779778823, rtol=1e-7)
+    # the fp32 evaluation (oracle dtype float32) against torch's fp32 sigmoid
+    z32 = np.linspace(-20.0, 20.0, 4001).astype(np.float32)
+    ours32 = sigmoid_to_f32(z32)
+    ref32 = torch.sigmoid(torch.as_tensor(z32)).numpy()
+    ulps32 = np.abs(ours32.view(np.int32).astype(np.int64) - ref32.view(np.int32).astype(np.int64))
+    assert ulps32.max() <= 4

@@ -65,3 +65,44 @@ def test_deferred_scores_equal_one_shot():
     assert len(seen) > 40
     for j, r in seen.items():
         assert abs(float(r) - float(one_shot[0, 0, j])) <= 1e-6, j
+
+
+@pytest.mark.parametrize("kind,T,n,s,w,C", [
+    ("flat", 30, 60, 2, 6, 5),       # one score level: the C earliest candidates stay forever
+    ("flat", 3, 40, 2, 5, 4),        # prompt shorter than the sink
+    ("level", 30, 160, 2, 6, 7),     # three levels: higher ones displace the latest lower one
+    ("level", 50, 200, 0, 9, 12),
+])
+def test_tied_scores_stepped_cache_equals_closed_form(kind, T, n, s, w, C):
+    """Exact ties: the explicit cache, stepped one token at a time from a prefill, holds at
+    every step the C best candidates by (score desc, index asc) of the brute-force closed
+    form -- among equal scores the lower index stays, and a token leaving the window
+    displaces the weakest entry (lowest score, then highest index) only with a strictly
+    higher score."""
+    from tests import ties
+    from tests.bruteforce import closed_form_retained
+    B, Hq, Hkv, D = 2, 4, 2, 16
+    make = ties.flat_case if kind == "flat" else ties.level_case
+    qt, kt, vt, cnn = make(300 + T, B, T + n, Hq, Hkv, D)
+    q, k, v = qt.float().numpy(), kt.float().numpy(), vt.float().numpy()
+    r = cnn_scores(k, v, cnn["W1"], cnn["b1"], cnn["W2"], cnn["b2"])
+    levels = np.unique(r[:, :, s:])
+    assert len(levels) == (1 if kind == "flat" else 3), levels
+    short = prefill(q[:, :T], k[:, :T], v[:, :T], s, w, C, cnn=cnn, rows=[])
+    cache = LayerCache.from_prefill(k[:, :T], v[:, :T], short["scores"], short["ends"],
+                                    s, w, C, cnn=cnn)
+    displaced = 0
+    for t in range(T, T + n):
+        before = [[set(cache.retained_indices(b, g).tolist()) for g in range(Hkv)]
+                  for b in range(B)]
+        cache.ingest(k[:, t], v[:, t])
+        for b in range(B):
+            for g in range(Hkv):
+                got = cache.retained_indices(b, g).tolist()
+                assert got == closed_form_retained(r[b, g], s, w, C, t), (t, b, g)
+                if len(before[b][g]) == C and set(got) != before[b][g]:
+                    displaced += 1
+    # the segment filled up; with levels, stronger newcomers displaced tied weaker entries
+    assert all(len(cache.ret[b][g]) == C for b in range(B) for g in range(Hkv))
+    if kind == "level":
+        assert displaced > 10
