@@ -15,13 +15,16 @@ this host.
 Beside it, the same engine as the two comparators of the LTE paper's Figure 4
 (sink + sliding-window attention with no retained segment, and full causal
 attention as a window covering the whole sequence), timed on the same inputs,
-a chunked prefill of the next 512 tokens onto the prompt's cache, and the
+a chunked prefill of the next 512 tokens onto the prompt's cache, the
 hybrid's linear-attention layer (B32, 4096 tokens, 16 heads of 128): chunked
-prefill and decode steps.
+prefill and decode steps, Figure 4(a)'s attention kernel with an artificial KV
+cache (B8, 10% retention), and the long-context shape (B4, 32768-token prompt,
+Hq32 Hkv8, w1024 C2048) at 5%, 20% and 50% retention: prefill and decode.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
                        [--no-cpu-baseline] [--no-decode] [--no-comparators]
-                       [--no-chunk] [--no-linear] [--copy-calibration MIB]
+                       [--no-chunk] [--no-linear] [--no-artificial] [--no-long]
+                       [--copy-calibration MIB]
 """
 from __future__ import annotations
 
@@ -68,6 +71,8 @@ def parse():
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-linear", action="store_true")
+    ap.add_argument("--no-artificial", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="sequences the oracle runs for the CPU baseline (0: one per core)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -185,6 +190,7 @@ def cpu_baseline(inp, wl, T, sample):
     dec_us = float(np.mean(per_seq_step)) * math.ceil(wl.B / used) * 1e6
     return {
         "value": nseq * T / wall, "unit": "tokens/s", "cores": used, "kind": "oracle",
+        "host_cores": cores,
         "sample": f"prefill of {nseq} of the {wl.B} sequences (all {wl.Hkv} KV heads, "
                   f"T={T}), one process per sequence; decode: {ndec} steps of {used} sequences, "
                   f"scaled to the full batch",
@@ -346,6 +352,146 @@ def linear_layer(dev, B=32, T=4096, H=16, D=128, ndec=64):
                                 "bytes_per_step": step_bytes}}
 
 
+def _attend_ms(layer, q, k, v, ws, out, reps=7):
+    """Median of event-timed lte_prefill_attend launches (each behind the gate)."""
+    import torch
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gate()
+        e0.record()
+        layer.prefill_attend(q, k, v, ws, out)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times[1:]))
+
+
+def artificial_cache(dev):
+    """Figure 4(a)'s kernel with an artificial KV cache: B8 T4096 Hq16 Hkv4 D128 s4 w512
+    C512, each out-of-window token retained with probability 0.1 (given as scores), the
+    attention alone; its MFMA fraction counted from the realised ranks."""
+    import torch
+    from learnable_kv_cache_amd import lte, synth
+    inp = synth.workload_inputs(2)
+    wl = inp["workload"]
+    B, T = wl.B, inp["T"]
+    layer = lte.Layer(lte.Config(B, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window, wl.capacity))
+    q, k, v = (inp[x].to(dev).contiguous() for x in ("q", "k", "v"))
+    ws = layer.alloc_workspace(T, dev)
+    out = torch.empty_like(q)
+    layer.prefill_select(T, ws, torch.as_tensor(inp["override"]).to(dev))
+    ms = _attend_ms(layer, q, k, v, ws, out)
+    rank = layer.workspace_views(ws, T)["rank"].cpu().numpy()
+    vis = visible_counts(rank, T, wl.sink, wl.window, wl.capacity)
+    flops = 4.0 * wl.D * (wl.Hq // wl.Hkv) * float(vis.sum())
+    return {"workload": f"attention-artificial-cache-b{B}-t{T} (10% Bernoulli retention)",
+            "attend_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "mean_visible_keys_per_row": float(vis.mean()),
+            "roofline": {"bound": "mfma", "kernel": "attend_prefill_kernel<128,4>",
+                         "achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                         "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+                         "flops_per_launch": flops}}
+
+
+def long_context(dev, rhos=(0.05, 0.2, 0.5)):
+    """The long-context stress shape: B4, 32768-token prompt, Hq32 Hkv8 D128 s4 w1024 C2048,
+    with one output bias per run chosen so that a fraction rho of the prompt's tokens
+    scores above 1/2 (from the quantile of the bias-free scores, computed by the library's
+    own scorer); per rho the whole prefill (tokens/s, the attention's MFMA fraction) and
+    256 decode steps over L rotating layer caches (us per layer-step, HBM fraction)."""
+    import torch
+    from learnable_kv_cache_amd import lte, synth
+    inp = synth.workload_inputs(5)
+    wl = inp["workload"]
+    B, T, ndec = wl.B, inp["T"], inp["steps"]
+    s, w, C, G = wl.sink, wl.window, wl.capacity, wl.Hq // wl.Hkv
+    layer = lte.Layer(lte.Config(B, wl.Hq, wl.Hkv, wl.D, s, w, C))
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    qp, kp, vp = (x[:, :T].contiguous() for x in (q, k, v))
+    dq = [q[:, T + t].contiguous() for t in range(ndec)]
+    dk = [k[:, T + t].contiguous() for t in range(ndec)]
+    dv = [v[:, T + t].contiguous() for t in range(ndec)]
+    ws = layer.alloc_workspace(T, dev)
+    out = torch.empty_like(qp)
+    layer.prefill_score(kp, vp, lte.CNN(inp["cnn"], dev), ws)      # b2 = 0
+    r0 = layer.workspace_views(ws, T)["scores"][:, :, s:].double().flatten()
+    cache_bytes = layer.cache_bytes()
+    L = math.ceil(2 * MALL_BYTES / cache_bytes) + 1
+    caches = [layer.alloc_cache(dev) for _ in range(L)]
+    res = {"workload": f"long-context-b{B}-t{T}", "B": B, "T": T, "Hq": wl.Hq, "Hkv": wl.Hkv,
+           "D": wl.D, "sink": s, "window": w, "capacity": C, "decode_steps": ndec,
+           "decode_layers": L, "runs": []}
+    for rho in rhos:
+        rq = float(torch.quantile(r0[:: max(1, r0.numel() // 4_000_000)], 1.0 - rho))
+        b2 = -math.log(rq / (1.0 - rq))
+        cnn = lte.CNN(dict(inp["cnn"], b2=np.full((wl.Hkv,), b2, np.float32)), dev)
+        times = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gate()
+            e0.record()
+            layer.prefill(qp, kp, vp, cnn=cnn, cache=caches[0], workspace=ws, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        pf_ms = float(np.median(times[1:]))
+        att_ms = _attend_ms(layer, qp, kp, vp, ws, out, reps=4)
+        views = layer.workspace_views(ws, T)
+        rank = views["rank"].cpu().numpy()
+        vis = visible_counts(rank, T, s, w, C)
+        flops = 4.0 * wl.D * G * float(vis.sum())
+        rate = float(views["ncand"].double().mean()) / (T - s)
+        # decode: every cache from this prefill, then a graph of ndec steps x L caches
+        for c in caches[1:]:
+            c.copy_(caches[0])
+        seed = caches[0].clone()
+        dout = torch.empty_like(dq[0])
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in caches:
+                layer.decode_step(dq[0], dk[0], dv[0], cnn, c, ws, dout)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in range(ndec):
+                for c in caches:
+                    layer.decode_step(dq[t], dk[t], dv[t], cnn, c, ws, dout)
+        flush = torch.empty(2 * MALL_BYTES, dtype=torch.uint8, device=dev)
+        us = []
+        for _ in range(3):
+            for c in caches:
+                c.copy_(seed)
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / (ndec * L))
+        us_step = float(np.median(us))
+        cnt = layer.cache_views(caches[-1])["count"].double().mean().item()
+        step_bytes = (B * wl.Hkv * (s + cnt + w) * wl.D * 2 * 2 + 2 * B * wl.Hq * wl.D * 2
+                      + 2 * B * wl.Hkv * wl.D * 2 + B * wl.Hkv * C * 4)
+        res["runs"].append({
+            "rho": rho, "b2": b2, "realised_candidate_rate": rate,
+            "prefill_ms": pf_ms, "prefill_tokens_per_s": B * T / (pf_ms * 1e-3),
+            "attend_ms": att_ms,
+            "attend_roofline": {"bound": "mfma", "achieved": flops / (att_ms * 1e-3) / 1e12,
+                                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                                "frac": flops / (att_ms * 1e-3) / PEAK_BF16_FLOPS},
+            "decode_us_per_step": us_step, "mean_segment_count": cnt,
+            "decode_roofline": {"bound": "hbm", "achieved": step_bytes / (us_step * 1e-6) / 1e9,
+                                "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                                "frac": step_bytes / (us_step * 1e-6) / PEAK_HBM_BPS,
+                                "bytes_per_step": step_bytes}})
+        del g, flush, seed
+        torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
@@ -442,17 +588,29 @@ def main():
     dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     stage_ms = {"score": [], "select": [], "attend": [], "build_cache": []}
     prefill_ms, dec_rot_ms, dec_warm_ms, step_ms = [], [], [], []
+    if not args.no_decode:
+        seed = torch.empty_like(cache0)
+        flush_buf = torch.empty(2 * MALL_BYTES, dtype=torch.uint8, device=dev)
     for it in range(args.warmup + args.steps):
         timed = it >= args.warmup
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         prefill_staged()
         if not args.no_decode:
+            # every decode replay starts from this prefill's cache (positions T .. T+ndec-1),
+            # untimed: the rotating caches are re-seeded, then the last-level cache is
+            # overwritten so that they start cold
+            seed.copy_(cache0)
+            for c in caches[1:]:
+                c.copy_(seed)
+            flush_buf.zero_()
             dev_ev[0].record(stream)
             graphs["rotating"].replay()
             dev_ev[1].record(stream)
-            graphs["warm"].replay()
+            caches[0].copy_(seed)
             dev_ev[2].record(stream)
+            graphs["warm"].replay()
+            dev_ev[3].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         if timed:
@@ -464,7 +622,7 @@ def main():
             prefill_ms.append(ev[0].elapsed_time(ev[4]))
             if not args.no_decode:
                 dec_rot_ms.append(dev_ev[0].elapsed_time(dev_ev[1]))
-                dec_warm_ms.append(dev_ev[1].elapsed_time(dev_ev[2]))
+                dec_warm_ms.append(dev_ev[2].elapsed_time(dev_ev[3]))
 
     # realised masks of the last prefill -> algorithmic work
     views = layer.workspace_views(ws, T)
@@ -511,7 +669,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill-b32-t4096 then decode-b32 (512 steps)", "B": B, "T": T,
+        "config": {"workload": f"prefill-b32-t4096 then decode-b32 (positions {T}-{T + ndec - 1})",
+                   "B": B, "T": T,
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "sink": wl.sink, "window": wl.window,
                    "capacity": wl.capacity, "decode_steps": ndec, "decode_layers": L},
         "prefill_ms": pf_ms,
@@ -527,6 +686,7 @@ def main():
         cv = layer.cache_views(caches[-1])
         counts = cv["count"].cpu().numpy()
         pos = int(cv["pos"].cpu().numpy().max())
+        assert pos == T + ndec, (pos, T + ndec)        # re-seeded before every replay
         nvis = float(counts.mean()) + wl.window + wl.sink
         step_bytes = (B * wl.Hkv * nvis * wl.D * 2 * 2 + 2 * B * wl.Hq * wl.D * 2
                       + 2 * B * wl.Hkv * wl.D * 2 + B * wl.Hkv * wl.capacity * 4)
@@ -535,7 +695,7 @@ def main():
         achieved_b = step_bytes / (us_rot * 1e-6)
         result["decode"] = {
             "us_per_step": us_rot, "warm_single_cache_us_per_step": us_warm,
-            "layers_rotated": L, "cache_bytes": cache_bytes, "approx_position": pos,
+            "layers_rotated": L, "cache_bytes": cache_bytes, "positions": [T, T + ndec - 1],
             "roofline": {"bound": "hbm", "achieved": achieved_b / 1e9,
                          "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                          "frac": achieved_b / PEAK_HBM_BPS, "bytes_per_step": step_bytes,
@@ -568,12 +728,18 @@ def main():
         del cws, cout
     if not args.no_linear:
         result["linear"] = linear_layer(dev)
+    if not args.no_artificial:
+        result["artificial_cache"] = artificial_cache(dev)
     if not args.no_comparators and not args.no_decode:
         cmp = comparators(inp, wl, T, dev, ndec=min(64, ndec))
         cmp["lte"] = {"window": wl.window, "capacity": wl.capacity, "prefill_attend_ms": att_ms,
                       "prefill_attend_tflops": achieved / 1e12,
                       "decode_us_per_step": result["decode"]["us_per_step"]}
         result["comparators"] = cmp
+    if not args.no_long:
+        del caches, graphs
+        torch.cuda.empty_cache()
+        result["long_context"] = long_context(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, T, args.cpu_sample)
     print(json.dumps(result), flush=True)

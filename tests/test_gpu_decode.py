@@ -301,7 +301,10 @@ def test_split_decode_repeats_bitwise():
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     dcnn = lte.CNN(cnn)
     ws = layer.alloc_workspace(T)
-    ca, cb = layer.alloc_cache(), layer.alloc_cache()
+    # zeroed blobs: slots a cache never wrote compare equal too
+    ca, cb = (torch.zeros(layer.cache_bytes(), dtype=torch.uint8, device="cuda") for _ in range(2))
+    for cache in (ca, cb):
+        layer.cache_init(cache)
     for cache in (ca, cb):
         layer.prefill(qd[:, :T].contiguous(), kd[:, :T].contiguous(), vd[:, :T].contiguous(),
                       cnn=dcnn, cache=cache, workspace=ws)
