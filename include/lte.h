@@ -35,7 +35,9 @@
  *     row-major.  bf16 tensors are passed as uint16_t bit patterns.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     legacy default stream) and never synchronises.  The library keeps no
- *     pointer after a call returns and holds no mutable global state.
+ *     pointer after a call returns and holds no mutable global state, except
+ *     the static device array of lte_decode_step_static (and its per-device
+ *     address).
  *   - Arguments are validated on the host before any launch; a failing call
  *     returns a status and leaves memory untouched.  A failed launch returns
  *     LTE_ERR_HIP.  No C++ exception crosses this interface.
@@ -63,7 +65,9 @@ typedef enum {
     LTE_ERR_UNSUPPORTED = 2,   /* valid but outside the supported range above */
     LTE_ERR_STATE = 3,         /* cache not in a state that allows the call   */
     LTE_ERR_HIP = 4,           /* a HIP launch or copy failed                 */
-    LTE_ERR_WORKSPACE = 5      /* workspace smaller than lte_workspace_bytes  */
+    LTE_ERR_WORKSPACE = 5,     /* workspace smaller than lte_workspace_bytes  */
+    LTE_ERR_SCRATCH = 6        /* more scratch than lte_decode_step_static's
+                                  static array holds                          */
 } lte_status;
 
 /* Layer shape. sink = s, window = w, capacity = C of the method. */
@@ -276,6 +280,20 @@ int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, void* cache,
 int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* k_t,
                     const uint16_t* v_t, const lte_cnn* cnn, void* cache, void* workspace,
                     size_t workspace_bytes, uint16_t* out_t, void* stream);
+
+/* lte_decode_step without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): identical results, bit for bit.  The split partials that
+ * lte_decode_step keeps in the workspace live instead in a static device array
+ * of 4 MiB (every supported shape needs at most about 3.2 MB; a larger need
+ * returns LTE_ERR_SCRATCH), one per device, whose address is looked up on the
+ * first call on each device.  The call allocates nothing.  Calls on one device
+ * share that array: calls that overlap in time on one device race (serialise
+ * them on one stream).  Nothing in the array needs clearing between calls:
+ * every split writes its partial before the last one reads it. */
+int lte_decode_step_static(const lte_config* cfg, const uint16_t* q_t, const uint16_t* k_t,
+                           const uint16_t* v_t, const lte_cnn* cnn, void* cache,
+                           uint16_t* out_t, void* stream);
 
 /* Copies the cache's bookkeeping into caller device buffers (parity, resume):
  * ret_idx int32 [B][Hkv][C], ret_score fp32 [B][Hkv][C], count int32

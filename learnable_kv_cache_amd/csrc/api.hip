@@ -124,6 +124,7 @@ const char* lte_status_string(int status) {
         case LTE_ERR_STATE: return "cache state does not allow this call";
         case LTE_ERR_HIP: return "HIP launch or copy failed";
         case LTE_ERR_WORKSPACE: return "workspace too small";
+        case LTE_ERR_SCRATCH: return "needs more scratch than the static array holds";
         default: return "unknown status";
     }
 }
@@ -396,6 +397,20 @@ int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* 
     if (workspace_bytes < ws_layout(sh, 0).total) return LTE_ERR_WORKSPACE;
     return hip_status(launch_decode(sh, true, q_t, k_t, v_t, cnn, cache_view(sh, cache),
                                     dec_part_ptr(sh, workspace), out_t, hipStream_t(stream)));
+}
+
+int lte_decode_step_static(const lte_config* cfg, const uint16_t* q_t, const uint16_t* k_t,
+                           const uint16_t* v_t, const lte_cnn* cnn, void* cache,
+                           uint16_t* out_t, void* stream) {
+    LTE_TRY(check_cfg(cfg));
+    LTE_TRY(check_cnn(cnn));
+    if (!q_t || !k_t || !v_t || !cache || !out_t) return LTE_ERR_INVALID_ARG;
+    Shape sh = make_shape(*cfg);
+    if (decode_part_bytes(sh) > kStaticScratchBytes) return LTE_ERR_SCRATCH;
+    float* part = nullptr;
+    if (static_scratch(&part) != hipSuccess) return LTE_ERR_HIP;
+    return hip_status(launch_decode(sh, true, q_t, k_t, v_t, cnn, cache_view(sh, cache), part,
+                                    out_t, hipStream_t(stream)));
 }
 
 int lte_cache_export(const lte_config* cfg, const void* cache, int32_t* ret_idx,

@@ -48,9 +48,38 @@
 //     call.
 // The partials bypass the non-coherent L2 copies instead of a cache-wide
 // write-back and invalidate, which a device-scope fence would cost on gfx950.
+#include <mutex>
+
 #include "score_core.h"
 
 namespace lte {
+
+// Split partials of lte_decode_step_static: a fixed device array instead of a
+// caller workspace, for callers that cannot allocate.  Every device the library
+// runs on holds its own copy until the process ends; host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol), only the
+// per-device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+hipError_t static_scratch(float** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float* ptrs[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {              // first call on this device, which is current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptrs[dev] = static_cast<float*>(p);
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -166,6 +166,16 @@ __host__ __device__ constexpr int decode_part_floats(int G, int D) {
     return G * D + ((2 * G + 3) & ~3);
 }
 
+// Bytes of the decode split partials (the only workspace a decode call uses).
+inline size_t decode_part_bytes(const Shape& sh) {
+    return align256(size_t(sh.B) * sh.Hkv * size_t(decode_nsplit(sh)) *
+                    decode_part_floats(sh.G, sh.D) * 4);
+}
+// Size of the static device array that holds them for lte_decode_step_static;
+// every supported shape needs at most about 3.2 MB (fewer than 128 (b, g) pairs
+// times at most 256 / (B Hkv) + 1 splits, 8320 bytes each).
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+
 struct WsLayout {
     size_t scores, rank, thr, ncand, w1p, select_scratch, dec_part, total;
 };
@@ -229,6 +239,9 @@ hipError_t launch_chunk_gather(const Shape& sh, int n, int Emax, const uint16_t*
                                const uint16_t* v, const CacheView& cache, const ChunkView& x,
                                float* ext_scores, uint16_t* ek, uint16_t* ev, hipStream_t st);
 hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_t st);
+// This device's address of the static split-partial array (kStaticScratchBytes),
+// looked up once per device with that device current.
+hipError_t static_scratch(float** out);
 hipError_t launch_score_evict(const Shape& sh, const lte_cnn& cnn, const uint16_t* k_t,
                               const uint16_t* v_t, const CacheView& cache, hipStream_t st);
 // ingest == false: attention over the cache as it is (lte_decode_attend);

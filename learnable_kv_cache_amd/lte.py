@@ -18,7 +18,8 @@ _lib = None
 
 LTE_OK = 0
 STATUS_NAMES = {0: "LTE_OK", 1: "LTE_ERR_INVALID_ARG", 2: "LTE_ERR_UNSUPPORTED",
-                3: "LTE_ERR_STATE", 4: "LTE_ERR_HIP", 5: "LTE_ERR_WORKSPACE"}
+                3: "LTE_ERR_STATE", 4: "LTE_ERR_HIP", 5: "LTE_ERR_WORKSPACE",
+                6: "LTE_ERR_SCRATCH"}
 
 
 class LTEError(RuntimeError):
@@ -85,6 +86,7 @@ SIGNATURES = {
     "lte_score_evict": (ctypes.c_int, [_CFG, _CNNP, _P, _P, _P, _P]),
     "lte_decode_attend": (ctypes.c_int, [_CFG, _P, _P, _P, _SZ, _P, _P]),
     "lte_decode_step": (ctypes.c_int, [_CFG, _P, _P, _P, _CNNP, _P, _P, _SZ, _P, _P]),
+    "lte_decode_step_static": (ctypes.c_int, [_CFG, _P, _P, _P, _CNNP, _P, _P, _P]),
     "lte_cache_export": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -317,6 +319,19 @@ class Layer:
                                      ctypes.byref(cnn.c), _ptr(cache), _ptr(workspace),
                                      int(workspace.numel()), _ptr(out_t), _stream()),
                "lte_decode_step")
+        return out_t
+
+    def decode_step_static(self, q_t, k_t, v_t, cnn: CNN, cache, out_t):
+        """lte_decode_step_static: one decode step with no workspace (the split partials
+        live in the library's static device array); out_t is caller-provided."""
+        c = self.cfg
+        _need(q_t, torch.bfloat16, (c.batch, c.q_heads, c.head_dim), "q_t")
+        _need(k_t, torch.bfloat16, (c.batch, c.kv_heads, c.head_dim), "k_t")
+        _need(v_t, torch.bfloat16, (c.batch, c.kv_heads, c.head_dim), "v_t")
+        _need(out_t, torch.bfloat16, (c.batch, c.q_heads, c.head_dim), "out_t")
+        _check(lib().lte_decode_step_static(ctypes.byref(self._c), _ptr(q_t), _ptr(k_t),
+                                            _ptr(v_t), ctypes.byref(cnn.c), _ptr(cache),
+                                            _ptr(out_t), _stream()), "lte_decode_step_static")
         return out_t
 
     def cache_views(self, cache) -> dict:

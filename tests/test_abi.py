@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     L = lte.lib()
     assert L.lte_version() == 1
-    for code in range(6):
+    for code in range(7):
         assert L.lte_status_string(code)
     assert L.lte_status_string(99) == b"unknown status"
 
@@ -107,6 +107,11 @@ def test_calls_fail_before_launch_on_bad_arguments():
     bad_cnn = lte._CNN(0x1000, 0, 0x1000, 0x1000)
     assert L.lte_score_evict(cfg, ctypes.byref(bad_cnn), fake, fake, fake, None) == 1
     assert L.lte_cache_init(cfg, None, None) == 1
+    # the decode step without a workspace: the same argument checks
+    SD = L.lte_decode_step_static
+    assert SD(cfg, fake, fake, fake, ctypes.byref(good_cnn), None, fake, None) == 1
+    assert SD(cfg, fake, fake, fake, ctypes.byref(bad_cnn), fake, fake, None) == 1
+    assert SD(cfg, fake, None, fake, ctypes.byref(good_cnn), fake, fake, None) == 1
     assert L.lte_cache_get_layout(cfg, None) == 1
 
 
