@@ -13,15 +13,14 @@
 //   * keys are processed in blocks of 64: first the band blocks, then the
 //     gathered columns below the band (sink + retained tokens alive at the
 //     tile's first row, via the per-head rank/thr lists), which are listed
-//     while the first band block loads.
+//     while the first band block loads.  Entries that every row of the tile
+//     sees come first, so only the last list blocks need a mask.
 //   * K/V tiles are double-buffered in LDS: the first by direct global->LDS
 //     loads, later ones fetched into registers one block ahead and stored to
 //     the free buffer at the end of the block, so one barrier per block
 //     suffices (with a direct load in flight the compiler would wait for all
 //     outstanding LDS reads before using any).  Scheduling groups keep three
 //     k-steps of K operands and four V operands in flight ahead of the MFMAs.
-//   * waves 0-3 hold a higher issue priority during q.k, so the two waves of a
-//     SIMD drift apart: one's softmax runs beside the other's MFMA work.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows from LDS are the A
 //     operand, each wave's 32 query rows stay in registers as the B operand.
 //     A lane then owns one query row, so the row max/sum of the online
@@ -34,9 +33,12 @@
 //     tensor its own pattern), so the row-strided MFMA operand reads hit
 //     distinct banks.
 //   * fp32 online softmax on raw logits, the 1/sqrt(D) scale and log2(e)
-//     folded into one FMA before exp2; masked keys are -inf; the reference
-//     maximum of a row moves only when exceeded by more than 2^8 in the
-//     exponent, so the running output is rarely rescaled.
+//     folded into one FMA before exp2; masked keys are -inf.  p is taken
+//     against a lazy reference maximum: a lane's sum of its block's p bounds
+//     each of them, so the block maximum is computed (and the reference moved,
+//     when exceeded by more than 2^8 in the exponent) only when that sum
+//     passes 2^8; the running output is rarely rescaled.
+//   * the output is staged through LDS and stored as whole rows.
 #include "lte_internal.h"
 
 namespace lte {
@@ -99,7 +101,8 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     constexpr int CPR = D / 8;              // 16-byte chunks per key row
     constexpr int TCH = 64 * CPR;           // chunks of one 64-key tile
     constexpr int LPW = TCH / 64 / NW;      // direct loads per wave per tile and tensor
-    constexpr int kMaxList = kMaxSink + kMaxCapacity;
+    constexpr int kMaxList = kMaxSink + kMaxCapacity + P;    // sink, retained, transient room
+    constexpr int kListTop = kMaxList - 1;
     constexpr int kBr = P > 64 ? P : 64;    // band keys whose rank can matter, rounded up
     static_assert(LPW >= 1 && LPW * 64 * NW == TCH, "tile split");
 
@@ -114,8 +117,8 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     __shared__ __align__(16) uint32_t lst[kMaxList];
     __shared__ __align__(16) int32_t brank[kBr];
     __shared__ int lfull[kMaxList / 64];            // list block visible to every row of the tile
-    __shared__ int wcnt[64];                        // per (pass slot, wave) counts
-    __shared__ int woff[65];                        // their exclusive prefix, then the total
+    __shared__ int wcnt[128];                       // per (pass slot, wave) counts: stable, transient
+    __shared__ int woff[130];                       // their exclusive prefixes, then the totals
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -233,7 +236,6 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const int p_row = rtile / G;
     const int hh = rtile % G;
     const int i_row = i0 + p_row;
-    const bool row_ok = i_row <= i_last && i_row >= qlo;
     const int irow = i_row <= i_last ? i_row : i_last;
     const int h = g * G + hh;
     bf16x8 qf[KK];
@@ -249,10 +251,15 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const float csc = kLog2e * rsqrtf(float(D));
 
     if (tid < kBr) brank[tid] = brv;
-    // ---- gathered columns below the band: sink, then the candidates alive at the
-    //      tile's first row, in index order (ballot compaction: order by pass slot
-    //      u, then wave, then lane, which is index order) ------------------------------
-    int len = ns;
+    // ---- gathered columns below the band: the sink, then the candidates alive at the
+    //      tile's first row.  Entries every row of the tile sees (rank within the last
+    //      row's threshold) come first, so the blocks they fill need no mask; the at
+    //      most P-1 entries that leave the retained set inside the tile follow them.
+    //      Ballot compaction (order by pass slot u, then wave, then lane); transient
+    //      entries are collected downward from the top of lst and moved after the
+    //      stable ones at the end -------------------------------------------------------
+    int len = ns;                                 // sink + stable entries so far
+    int ntr = 0;                                  // transient entries so far
     for (int j = tid; j < ns; j += NT) lst[j] = uint32_t(j);           // field 0: always visible
     for (int base = s; base < band_lo; base += LU * NT) {
         if (base != s) {
@@ -265,33 +272,48 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         uint32_t pre[LU];
 #pragma unroll
         for (int u = 0; u < LU; ++u) {
-            const unsigned long long m = __ballot(rr[u] <= thr0);
+            const bool st = rr[u] <= thr_last;
+            const bool tr = !st && rr[u] <= thr0;
+            const unsigned long long ms = __ballot(st);
+            const unsigned long long mt = __ballot(tr);
+            const unsigned long long m = st ? ms : mt;
             pre[u] = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
                                                __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-            if (lane == 0) wcnt[u * NW + wave] = __popcll(m);
+            if (lane == 0) {
+                wcnt[u * NW + wave] = __popcll(ms);
+                wcnt[64 + u * NW + wave] = __popcll(mt);
+            }
         }
         __syncthreads();
-        if (wave == 0) {                          // exclusive scan of the 64 counts
-            const int c = wcnt[lane];
+        if (wave < 2) {                           // exclusive scans of the 64 + 64 counts
+            const int c = wcnt[wave * 64 + lane];
             int incl = c;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
                 const int y = __shfl_up(incl, d, 64);
                 if (lane >= d) incl += y;
             }
-            woff[lane] = incl - c;
-            if (lane == 63) woff[64] = incl;
+            woff[wave * 65 + lane] = incl - c;
+            if (lane == 63) woff[wave * 65 + 64] = incl;
         }
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < LU; ++u) {
-            if (rr[u] <= thr0)
-                lst[len + woff[u * NW + wave] + int(pre[u])] =
-                    (uint32_t(rr[u] + 1) << 16) | uint32_t(base + u * NT + tid);
+            const uint32_t ent = (uint32_t(rr[u] + 1) << 16) | uint32_t(base + u * NT + tid);
+            if (rr[u] <= thr_last)
+                lst[len + woff[u * NW + wave] + int(pre[u])] = ent;
+            else if (rr[u] <= thr0)
+                lst[kListTop - (ntr + woff[65 + u * NW + wave] + int(pre[u]))] = ent;
         }
         len += woff[64];
+        ntr += woff[65 + 64];
         __syncthreads();                          // wcnt and woff are reused
     }
+    // transient entries after the stable ones (the regions do not overlap: len + ntr <=
+    // s + C and ntr < P, while lst holds s + C + P entries)
+    for (int e = tid; e < ntr; e += NT) lst[len + e] = lst[kListTop - e];
+    len += ntr;
+    __syncthreads();
     // pad to whole blocks with entries no row sees (field 0xffff, key 0)
     for (int e = len + tid; e < ((len + 63) & ~63); e += NT) lst[e] = 0xffff0000u;
     const int nlist = (len + 63) / 64;
@@ -336,7 +358,6 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         const int jb0 = band_lo + blk * 64;                // first key of a band block
 
         // ---- S^T = K Q^T for 64 keys x this wave's 32 rows -----------------------
-        if (wave < NW / 2) __builtin_amdgcn_s_setprio(2);
         f32x16 sacc[2];
         sacc[0] = f32x16{};
         sacc[1] = f32x16{};
@@ -359,7 +380,6 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
-        __builtin_amdgcn_s_setprio(0);
         // ---- mask in place: element e of subtile ks is key slot
         //      ks*32 + (e/4)*8 + half*4 + e%4 of this block ----------------------------
         const bool list_full =
@@ -428,39 +448,59 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         }
 
         // ---- online softmax in raw logits, scale folded into the exponent; row =
-        //      this lane's query, keys split with lane^32.  The reference maximum
-        //      m_run moves only when a row's maximum exceeds it by more than 2^8 in
-        //      the exponent, so p <= 256 and the output is rarely rescaled; the
-        //      final division by l_run cancels the choice of m_run exactly.
-        float mloc = sacc[0][0];
+        //      this lane's query, keys split with lane^32.  p is taken against the
+        //      reference m_run; the lane's block sum bounds every p, so the row
+        //      maximum is needed only when that sum exceeds 2^8 (a new maximum, or
+        //      inf/NaN) or the row has no reference yet.  m_run then moves only when
+        //      exceeded by more than 2^8 in the exponent, so p <= 256 and the output
+        //      is rarely rescaled; the final division by l_run cancels the choice of
+        //      m_run exactly.
+        float moff = (m_run == -INFINITY) ? 0.0f : -m_run * csc;
+        float pv[32];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[ks][e]);
-        const float mrow = max_xor32(mloc);
-        // NaN (both -inf: nothing visible yet) compares false: no move
-        const bool move = (mrow - m_run) * csc > 8.0f;
-        if (__ballot(move) != 0ull) {
+            for (int e = 0; e < 16; ++e) pv[ks * 16 + e] = fast_exp2(fmaf(sacc[ks][e], csc, moff));
+        auto tree = [&]() {
+            float t[16];
+#pragma unroll
+            for (int x = 0; x < 16; ++x) t[x] = pv[2 * x] + pv[2 * x + 1];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) t[x] = t[2 * x] + t[2 * x + 1];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) t[x] = t[2 * x] + t[2 * x + 1];
+            return (t[0] + t[1]) + (t[2] + t[3]);
+        };
+        float lsum = tree();
+        // the fast path needs a finite reference: until a row has seen a visible key
+        // its reference is undefined (and p was taken against 0)
+        if (__ballot(!(lsum <= 256.0f) || m_run == -INFINITY) != 0ull) {
+            float mloc = sacc[0][0];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[ks][e]);
+            const float mrow = max_xor32(mloc);
+            // NaN (both -inf: nothing visible yet) compares false: no move
+            const bool move = (mrow - m_run) * csc > 8.0f;
             const float m_new = move ? mrow : m_run;
             const float alpha = move ? fast_exp2((m_run - m_new) * csc) : 1.0f;
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
             m_run = m_new;
-        }
-        const float moff = (m_run == -INFINITY) ? 0.0f : -m_run * csc;
-        float lsum = 0.0f;
-        bf16x8 pf[4];
+            moff = (m_run == -INFINITY) ? 0.0f : -m_run * csc;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = fast_exp2(fmaf(sacc[ks][e], csc, moff));
-                lsum += p;
-                pf[ks * 2 + (e >> 3)][e & 7] = (__bf16)p;
-            }
+                for (int e = 0; e < 16; ++e)
+                    pv[ks * 16 + e] = fast_exp2(fmaf(sacc[ks][e], csc, moff));
+            lsum = tree();
         }
         l_run += lsum;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int x = 0; x < 32; ++x) pf[x >> 3][x & 7] = (__bf16)pv[x];
 
         // ---- O^T += V^T P^T ------------------------------------------------------
         // operand element e of lane (16-group G, index i) is V[key][dt*32 + (G&1)*16 + i]
@@ -507,11 +547,18 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
 #undef LTE_FETCH
 #undef LTE_STORE
 
-    // ---- normalise and store: element e of d-tile dt is dim dt*32 + (e/4)*8 + half*4 + e%4
-    const float l_tot = add_xor32(l_run);
-    if (row_ok) {
-        const float inv = 1.0f / l_tot;
-        uint16_t* orow = out + ((long(b) * qrows + (i_row - qlo)) * Hq + h) * D;
+    // ---- normalise, stage the wave's 32 rows as bf16 in LDS (the K/V tiles are free
+    //      after the last block's barrier), then store whole rows: the G heads of one
+    //      position are G*D contiguous elements of out, so 64 lanes write 1 KB runs
+    //      instead of 32 rows x 16 bytes per store.  Element e of d-tile dt is dim
+    //      dt*32 + (e/4)*8 + half*4 + e%4; the staged row r holds its 16-byte piece c at
+    //      position c ^ (r mod CPR), so the 32 rows of one write spread over the banks.
+    const float inv = 1.0f / add_xor32(l_run);
+    constexpr int SROW = CPR * 16;                // staged bytes per row
+    char* stg = reinterpret_cast<char*>(wave < 2 ? K0 : (wave < 4 ? V0 : (wave < 6 ? K1 : V1))) +
+                (wave & 1) * 32 * SROW;
+    {
+        const int r = lane & 31;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -519,9 +566,25 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
                 bf16x4 o4;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) o4[u] = (__bf16)(acc_o[dt][e4 * 4 + u] * inv);
-                *reinterpret_cast<bf16x4*>(orow + dt * 32 + e4 * 8 + half * 4) = o4;
+                *reinterpret_cast<bf16x4*>(stg + r * SROW + (((dt * 4 + e4) ^ (r & (CPR - 1))) * 16) +
+                                           half * 8) = o4;
             }
         }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int x = 0; x < 32 * CPR / 64; ++x) {
+        const int c = x * 64 + lane;
+        const int rr = c / CPR;                   // staged row: tile row wave*32 + rr
+        const int ch = c % CPR;
+        const int rt = wave * 32 + rr;
+        const int i = i0 + rt / G;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + rr * SROW + ((ch ^ (rr & (CPR - 1))) * 16));
+        if (i <= i_last && i >= qlo)
+            *reinterpret_cast<u32x4*>(out + ((long(b) * qrows + (i - qlo)) * Hq + g * G + rt % G) * D +
+                                      ch * 8) = val;
     }
 }
 
