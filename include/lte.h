@@ -6,9 +6,11 @@
  * Hybrid Sparse Attention and Contextualized Learnable Token Eviction"
  * (He & Garner, arXiv 2510.20787), summary page:
  *   - Figure 2 caption: attention sink of size s, sliding window of size w,
- *     a CNN that predicts a per-token, per-head retention score r_{j,h} from
- *     past and future neighbours, eviction decided when a KV pair leaves the
- *     window, and the resulting per-head "A-plus-column" sparsity pattern.
+ *     a small convolutional network over each token's nearby past and future
+ *     keys/values whose output r_{j,h} (one number per token and head) rates
+ *     how well worth keeping the token is; eviction decided when a KV pair
+ *     leaves the window, and the resulting per-head "A-plus-column" sparsity
+ *     pattern.
  *   - Figure 3 caption: cache layout with a circular window segment and an
  *     out-of-window segment of capped capacity for retained KVs and the sink;
  *     scoring batched and deferred as late as possible.
@@ -247,7 +249,12 @@ int lte_prefill_build_cache(const lte_config* cfg, int64_t T, const uint16_t* k,
                             void* cache, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Ingest one token per sequence (position t = pos):
+ * Ingest one token per sequence (position t = pos).  Figure 2 caption of the
+ * learnable-eviction paper: a token is kept or dropped when it leaves the
+ * sliding window, by its retention score, with at most C kept per head;
+ * Figure 3 caption: the window is a circular segment of the cache, retained
+ * tokens sit in a capped out-of-window segment, and scoring is batched and
+ * put off until the last step at which the CNN's inputs are still cached.
  *   1. the token t-w leaves ring slot t mod w; if t-w >= s and its score is
  *      > 0.5 it enters the retained segment, displacing the weakest entry
  *      (lowest score, then highest index) when the segment already holds C
@@ -264,7 +271,9 @@ int lte_score_evict(const lte_config* cfg, const lte_cnn* cnn, const uint16_t* k
                     const uint16_t* v_t, void* cache, void* stream);
 
 /* Attention of the newest token's queries q_t (bf16 [B][Hq][D]) over the
- * cache: sink U retained segment U ring, out_t bf16 [B][Hq][D].  Requires
+ * cache: sink U retained segment U ring, out_t bf16 [B][Hq][D] (Figure 2
+ * caption: each head attends to its sink, its window and the tokens it kept;
+ * Abstract: so a decode step costs the same at any position).  Requires
  * pos >= 1 (LTE_ERR_STATE is not detectable on the host: a cache with
  * pos == 0 yields zeros).  The cache's arrive words are used during the
  * call and left at 0; nothing else in the cache changes. */
@@ -272,7 +281,9 @@ int lte_decode_attend(const lte_config* cfg, const uint16_t* q_t, void* cache,
                       void* workspace, size_t workspace_bytes, uint16_t* out_t, void* stream);
 
 /* One decode step, with the result of lte_score_evict followed by
- * lte_decode_attend, in one launch: the splits of the cache (64 slots each)
+ * lte_decode_attend, in one launch (Figure 3 caption: the step reads and
+ * updates the cache of Figure 3's layout in place, at constant cost per
+ * token): the splits of the cache (64 slots each)
  * are read in their pre-step state with the new token and the segment slot
  * the leaving token takes substituted; the last split of a (batch, KV head)
  * to finish merges the partial softmax sums in split order and then updates
@@ -296,8 +307,12 @@ int lte_decode_step_static(const lte_config* cfg, const uint16_t* q_t, const uin
                            uint16_t* out_t, void* stream);
 
 /* Copies the cache's bookkeeping into caller device buffers (parity, resume):
+ * the out-of-window segment of Figure 3's caption (which tokens it holds and
+ * their retention scores), its fill and the position.
  * ret_idx int32 [B][Hkv][C], ret_score fp32 [B][Hkv][C], count int32
- * [B][Hkv], pos int64 [B][Hkv].  Any pointer may be NULL to skip it. */
+ * [B][Hkv], pos int64 [B][Hkv].  Slots x >= count hold unspecified values;
+ * slots below count are in no particular order.  Plain device-to-device
+ * copies on the stream.  Any pointer may be NULL to skip it. */
 int lte_cache_export(const lte_config* cfg, const void* cache, int32_t* ret_idx,
                      float* ret_score, int32_t* count, int64_t* pos, void* stream);
 

@@ -1,8 +1,9 @@
 // Retention scoring CNN over a whole prompt on gfx950.
 //
-// LTE paper (arXiv 2510.20787) summary page, Figure 2 caption: a CNN stack
-// reads the keys/values of short-range past and future neighbours and
-// predicts a per-token, per-head retention score r_{j,h}.  Shape used here:
+// LTE paper (arXiv 2510.20787) summary page, Figure 2 caption: the
+// retention score r_{j,h} of token j in head h comes from a stack of
+// convolutions over the keys/values of the few tokens on either side of j.
+// Shape used here:
 // per KV head, conv1d(2D -> 32, kernel 3, zero pad 1) over concat(k, v),
 // GELU, conv1d(32 -> 1, kernel 3, zero pad 1), sigmoid.  x is bf16 (the
 // layer's input dtype), W1 is rounded to bf16, accumulation is fp32; the GELU
