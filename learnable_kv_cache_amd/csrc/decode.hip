@@ -312,6 +312,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     static_assert(G * D * 4 <= TL::kKW * 16 && 2 * G * 4 <= TL::kVW * 16, "wave partials fit");
     __shared__ __align__(16) u32x4 Ks[NW][TL::kKW];
     __shared__ __align__(16) u32x4 Vs[NW][TL::kVW];
+    __shared__ __align__(16) u32x4 Kx[TL::kTile];     // wave 0's prefetched last chunk
+    __shared__ __align__(16) u32x4 Vx[TL::kTile];
     __shared__ float wk_sc[NW];
     __shared__ int wk_tk[NW], wk_sl[NW];
     __shared__ int last_flag;
@@ -321,10 +323,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int q16 = lane >> 4;
-    const int sp = blockIdx.x % nsplit;
-    const int bg = blockIdx.x / nsplit;
+    const int sp = __builtin_amdgcn_readfirstlane(blockIdx.x % nsplit);
+    const int bg = __builtin_amdgcn_readfirstlane(blockIdx.x / nsplit);
     const int b = bg / Hkv;
     const int g = bg % Hkv;
+    // the state first (scalar loads; positions fit in 32 bits)
+    const int p = int(c.pos[bg]);
+    const int cnt = c.count[bg];
+    const int X = INGEST ? c.nx_slot[bg] : -1;
+    const int u = INGEST ? int(c.next_unscored[bg]) : 0;
+    const float rl = INGEST ? c.nx_score[bg] : 0.0f;
     u32x4* Kt = Ks[wave];
     u32x4* Vt = Vs[wave];
     const long base = long(bg) * S * D;
@@ -349,15 +357,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         const int pidx = 64 * x + lane;
         return vb + roff[x] + 16 * ((pidx % CPR) ^ vswz<D>(pidx / CPR));
     };
-    auto load_lds = [&](const uint32_t (&roff)[NL]) {
+    auto load_lds = [&](const uint32_t (&roff)[NL], u32x4* Kd, u32x4* Vd) {
 #pragma unroll
         for (int x = 0; x < NL; ++x) {
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)kaddr(roff, x),
-                (__attribute__((address_space(3))) void*)(&Kt[64 * x]), 16, 0, 0);
+                (__attribute__((address_space(3))) void*)(&Kd[64 * x]), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)vaddr(roff, x),
-                (__attribute__((address_space(3))) void*)(&Vt[64 * x]), 16, 0, 0);
+                (__attribute__((address_space(3))) void*)(&Vd[64 * x]), 16, 0, 0);
         }
     };
     // ring chunk i: slots s+C+32i .. (rows past the ring re-read its last slot)
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     if (early0) {
         uint32_t roff[NL];
         ring_rows(ent0, roff);
-        load_lds(roff);
+        load_lds(roff, Kt, Vt);
     }
     // the segment's scores and tokens, for the weakest entry after the ingest
     float sc_e[kScan];
@@ -406,12 +414,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         nvv = *reinterpret_cast<const u32x4*>(v_t + long(bg) * D + lane * 8);
     }
 
-    // ---- the state (positions fit in 32 bits) and the visible rows ----------------------
-    const int p = int(c.pos[bg]);
-    const int cnt = c.count[bg];
-    const int X = INGEST ? c.nx_slot[bg] : -1;
-    const int u = INGEST ? int(c.next_unscored[bg]) : 0;
-    const float rl = INGEST ? c.nx_score[bg] : 0.0f;
+    // ---- the visible rows ------------------------------------------------------------------
     const int t = INGEST ? p : p - 1;
     const int tslot = t >= 0 ? t % w : 0;
     const int new_cnt = (X >= 0 && X == cnt) ? cnt + 1 : cnt;
@@ -455,7 +458,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     if (!early0 && ent0 < e_hi) {
         uint32_t roff[NL];
         chunk_rows(ent0, roff);
-        load_lds(roff);
+        load_lds(roff, Kt, Vt);
+    }
+    // When the last round of the list would hold one chunk (wave 0's), that chunk loads
+    // now into a tile pair of its own and is consumed right after wave 0's first, so no
+    // round waits on a single chunk.
+    const int n_ent = e_hi - e_lo;
+    const bool xtra = n_ent > NW && n_ent % NW == 1;
+    const int e_rr = xtra ? e_hi - 1 : e_hi;                    // entries dealt round-robin
+    if (xtra && wave == 0) {
+        uint32_t roff[NL];
+        chunk_rows(e_hi - 1, roff);
+        load_lds(roff, Kx, Vx);
     }
     // ingest operands consumed at the end: the score of the token leaving at the next
     // step and the leaving token's row (lanes < D/8 of wave 0)
@@ -502,8 +516,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{};
     typedef short v4i16 __attribute__((ext_vector_type(4)));
-    for (int ent = ent0; ent < e_hi; ent += NW) {
-        __builtin_amdgcn_s_waitcnt(0);        // this chunk's direct loads have landed
+    auto consume = [&](int ent, u32x4* Kc, u32x4* Vc) {
         const bool is_ring = ent < nr;
         const int k0 = is_ring ? RW * ent : RW * head_chunk(ent - nr);   // first row / slot
         // visible rows of the chunk as a bit mask (lane j < 32 tests row k0 + j)
@@ -518,7 +531,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
 #pragma unroll
                 for (int x = 0; x < NL; ++x) {
                     const int pidx = 64 * x + lane;
-                    if (!((vmask >> (pidx / CPR)) & 1u)) Vt[pidx] = u32x4{};
+                    if (!((vmask >> (pidx / CPR)) & 1u)) Vc[pidx] = u32x4{};
                 }
             }
             if (INGEST && t >= s) pr = tslot - k0;
@@ -526,8 +539,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
             pr = t - k0;
         }
         if (INGEST && pr >= 0 && pr < RW && lane < CPR) {
-            Kt[pr * CPR + (lane ^ kswz<D>(pr))] = nk;
-            Vt[pr * CPR + (lane ^ vswz<D>(pr))] = nvv;
+            Kc[pr * CPR + (lane ^ kswz<D>(pr))] = nk;
+            Vc[pr * CPR + (lane ^ vswz<D>(pr))] = nvv;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -541,7 +554,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, Kt[row * CPR + ((4 * kk + q16) ^ kswz<D>(row))]);
+                    bf16x8, Kc[row * CPR + ((4 * kk + q16) ^ kswz<D>(row))]);
                 sacc[mt] = mfma16(a, qf[kk], sacc[mt]);
             }
         }
@@ -590,7 +603,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
                 const int key = 16 * r2 + 4 * q16 + (l16 >> 2);
                 const int d0 = 16 * dt + 4 * (l16 & 3);
                 const __bf16* src = reinterpret_cast<const __bf16*>(
-                                        &Vt[key * CPR + ((d0 >> 3) ^ vswz<D>(key))]) + (d0 & 7);
+                                        &Vc[key * CPR + ((d0 >> 3) ^ vswz<D>(key))]) + (d0 & 7);
                 const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) v4i16*)(src));
                 const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
@@ -599,12 +612,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
             }
             oacc[dt] = mfma16(a, pf, oacc[dt]);
         }
+    };
+    bool xpend = xtra && wave == 0;
+    for (int ent = ent0; ent < e_rr; ent += NW) {
+        __builtin_amdgcn_s_waitcnt(0);        // this chunk's direct loads have landed
+        consume(ent, Kt, Vt);
         // the next chunk's rows into the tiles once their reads are done
-        if (ent + NW < e_hi) {
+        if (ent + NW < e_rr) {
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
             uint32_t roff[NL];
             chunk_rows(ent + NW, roff);
-            load_lds(roff);
+            load_lds(roff, Kt, Vt);
+        }
+        if (xpend) {                          // landed with the first chunk
+            xpend = false;
+            consume(e_hi - 1, Kx, Vx);
         }
     }
     l_run += __shfl_xor(l_run, 16, 64);
@@ -619,8 +641,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
     }
 
     // ---- the waves' partials combine in LDS: wave wv's o [G][D] in its K region,
-    //      (max, sum) of head h (log2 units) at 2h of its V region ----------------------------
-    __syncthreads();                              // every tile and scorer row is free
+    //      (max, sum) of head h (log2 units) at 2h of its V region (the wave's own tiles,
+    //      free once its last chunk and scorer rows are consumed) -------------------------
     if (l16 < G) {
         float* po = reinterpret_cast<float*>(Kt);
 #pragma unroll
@@ -663,18 +685,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         for (int e = 0; e < DPL; ++e) ov[e] = po[hh * D + d0 + e];
         merge_in(pm[2 * hh], pm[2 * hh + 1], ov);
     }
-    // the weakest entry of the post-step segment, over the waves in order
+    // the weakest entry of the post-step segment over the waves' candidates (tokens are
+    // distinct, so the order is total and any reduction order gives the same entry);
+    // only wave 0 commits
     float wsc = INFINITY;
     int wtk = -1, wsl = -1;
-    if (INGEST) {
-#pragma unroll
-        for (int wv = 0; wv < NW; ++wv) {
-            if (weaker(wk_sc[wv], wk_tk[wv], wsc, wtk)) {
-                wsc = wk_sc[wv];
-                wtk = wk_tk[wv];
-                wsl = wk_sl[wv];
-            }
+    if (INGEST && wave == 0) {
+        if (lane < NW) {
+            wsc = wk_sc[lane];
+            wtk = wk_tk[lane];
+            wsl = wk_sl[lane];
         }
+        wave_weakest(wsc, wtk, wsl);
     }
 
     if (nsplit > 1) {
