@@ -296,7 +296,7 @@ int lte_decode_step(const lte_config* cfg, const uint16_t* q_t, const uint16_t* 
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): identical results, bit for bit.  The split partials that
  * lte_decode_step keeps in the workspace live instead in a static device array
- * of 4 MiB (every supported shape needs at most about 3.2 MB; a larger need
+ * of 5 MiB (every supported shape needs at most about 4.3 MB; a larger need
  * returns LTE_ERR_SCRATCH), one per device, whose address is looked up on the
  * first call on each device.  The call allocates nothing.  Calls on one device
  * share that array: calls that overlap in time on one device race (serialise

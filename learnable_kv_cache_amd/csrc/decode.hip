@@ -26,13 +26,16 @@
 // one (nx_slot, nx_score): the attention of a step never waits for it.
 //
 // A decode step is one launch.  Each (batch, KV head) is served by one
-// workgroup of 8 waves, or, when there are fewer than 128 such pairs, by a few
+// workgroup of 8 waves, or, when there are fewer than 256 such pairs, by a few
 // workgroups that split its visible rows:
 //   * the visible rows (sink, post-step segment, window) are read in chunks of
 //     32 by direct global->LDS loads of whole 256-byte rows, so only occupied
-//     slots cost bandwidth.  Rows that differ in the post-ingest state are
-//     read from where they are before the step: the new token from the k_t/v_t
-//     inputs, the leaving token (taking segment slot X) from its ring slot;
+//     slots cost bandwidth.  A wave refills its K tile with its next chunk as
+//     soon as the q.k operands are in registers and its V tile as soon as the
+//     p.v operands are, so its loads are in flight while it computes.  Rows
+//     that differ in the post-ingest state are read from where they are before
+//     the step: the new token from the k_t/v_t inputs, the leaving token
+//     (taking segment slot X) from its ring slot;
 //   * q.k and p.v run on v_mfma_f32_16x16x32_bf16 with the G <= 16 query heads
 //     of the KV head as the 16 columns; V is read back transposed
 //     (ds_read_b64_tr_b16);
@@ -357,16 +360,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         const int pidx = 64 * x + lane;
         return vb + roff[x] + 16 * ((pidx % CPR) ^ vswz<D>(pidx / CPR));
     };
-    auto load_lds = [&](const uint32_t (&roff)[NL], u32x4* Kd, u32x4* Vd) {
+    auto load_k = [&](const uint32_t (&roff)[NL], u32x4* Kd) {
 #pragma unroll
-        for (int x = 0; x < NL; ++x) {
+        for (int x = 0; x < NL; ++x)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)kaddr(roff, x),
                 (__attribute__((address_space(3))) void*)(&Kd[64 * x]), 16, 0, 0);
+    };
+    auto load_v = [&](const uint32_t (&roff)[NL], u32x4* Vd) {
+#pragma unroll
+        for (int x = 0; x < NL; ++x)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)vaddr(roff, x),
                 (__attribute__((address_space(3))) void*)(&Vd[64 * x]), 16, 0, 0);
-        }
+    };
+    auto load_lds = [&](const uint32_t (&roff)[NL], u32x4* Kd, u32x4* Vd) {
+        load_k(roff, Kd);
+        load_v(roff, Vd);
     };
     // ring chunk i: slots s+C+32i .. (rows past the ring re-read its last slot)
     auto ring_rows = [&](int i, uint32_t (&roff)[NL]) {
@@ -516,7 +526,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{};
     typedef short v4i16 __attribute__((ext_vector_type(4)));
-    auto consume = [&](int ent, u32x4* Kc, u32x4* Vc) {
+    // nxt >= 0: the entry whose rows replace this chunk's in the same tiles, K as soon as
+    // the q.k operands are read, V as soon as the p.v operands are
+    auto consume = [&](int ent, u32x4* Kc, u32x4* Vc, int nxt) {
+        uint32_t nroff[NL];
+        if (nxt >= 0) chunk_rows(nxt, nroff);
         const bool is_ring = ent < nr;
         const int k0 = is_ring ? RW * ent : RW * head_chunk(ent - nr);   // first row / slot
         // visible rows of the chunk as a bit mask (lane j < 32 tests row k0 + j)
@@ -546,17 +560,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // s^T = K q^T: rows = keys 16mt + 4q16 + r of the chunk, column = head l16
+        bf16x8 ka[2][KS];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int row = 16 * mt + l16;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                ka[mt][kk] = __builtin_bit_cast(
+                    bf16x8, Kc[row * CPR + ((4 * kk + q16) ^ kswz<D>(row))]);
+        }
+        if (nxt >= 0) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the K tile is read
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(nroff, Kc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         f32x4 sacc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             sacc[mt] = f32x4{};
-            const int row = 16 * mt + l16;
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, Kc[row * CPR + ((4 * kk + q16) ^ kswz<D>(row))]);
-                sacc[mt] = mfma16(a, qf[kk], sacc[mt]);
-            }
+            for (int kk = 0; kk < KS; ++kk) sacc[mt] = mfma16(ka[mt][kk], qf[kk], sacc[mt]);
         }
         if (vmask != 0xffffffffu) {
             const uint32_t lm = vmask >> (4 * q16);
@@ -595,9 +619,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         // o^T += V^T p^T: rows = dims 16dt + 4q16 + r, column = head l16.  A operand
         // element e of lane (q16, i): V[16(e/4) + 4q16 + e%4][16dt + i], two transposing
         // reads of 4 keys; lane j of 16 reads key .. + j/4, dims 16dt + 4(j%4) .. +3
+        bf16x8 va[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            bf16x8 a;
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2) {
                 const int key = 16 * r2 + 4 * q16 + (l16 >> 2);
@@ -608,25 +632,25 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
                     (__attribute__((address_space(3))) v4i16*)(src));
                 const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a[4 * r2 + e] = b4[e];
+                for (int e = 0; e < 4; ++e) va[dt][4 * r2 + e] = b4[e];
             }
-            oacc[dt] = mfma16(a, pf, oacc[dt]);
         }
+        if (nxt >= 0) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the V tile is read
+            __builtin_amdgcn_sched_barrier(0);
+            load_v(nroff, Vc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma16(va[dt], pf, oacc[dt]);
     };
     bool xpend = xtra && wave == 0;
     for (int ent = ent0; ent < e_rr; ent += NW) {
         __builtin_amdgcn_s_waitcnt(0);        // this chunk's direct loads have landed
-        consume(ent, Kt, Vt);
-        // the next chunk's rows into the tiles once their reads are done
-        if (ent + NW < e_rr) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-            uint32_t roff[NL];
-            chunk_rows(ent + NW, roff);
-            load_lds(roff, Kt, Vt);
-        }
+        consume(ent, Kt, Vt, ent + NW < e_rr ? ent + NW : -1);
         if (xpend) {                          // landed with the first chunk
             xpend = false;
-            consume(e_hi - 1, Kx, Vx);
+            consume(e_hi - 1, Kx, Vx, -1);
         }
     }
     l_run += __shfl_xor(l_run, 16, 64);
@@ -747,13 +771,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         }
     }
 
-    // ---- o_t, then the rest of the ingest ----------------------------------------------
-    if (active) {
-        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-        __bf16* orow = reinterpret_cast<__bf16*>(out_t) + (long(b) * Hq + g * G + hh) * D + d0;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(o[e] * inv);
-    }
+    // ---- the ingest (its stores wait on nothing outstanding), then o_t -------------------
     if (INGEST && wave == 0) {
         // the leaving token's row into its segment slot; no workgroup reads that slot's
         // old contents in this step, and every read of the ring slot is complete
@@ -763,6 +781,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
             *reinterpret_cast<u32x4*>(c.v + dst) = lv;
         }
         ingest_commit<D>(c, bg, s, w, C, S, t, cnt, X, rl, u, wsl, wsc, r1, nk, nvv);
+    }
+    if (active) {
+        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+        __bf16* orow = reinterpret_cast<__bf16*>(out_t) + (long(b) * Hq + g * G + hh) * D + d0;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(o[e] * inv);
     }
     if (nsplit > 1 && tid == 0)
         __hip_atomic_store(c.arrive + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

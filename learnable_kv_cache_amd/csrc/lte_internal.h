@@ -150,13 +150,14 @@ inline size_t select_scratch_words(int64_t T) {
 }
 
 // Decode split-K.  A workgroup (8 waves) attends over a contiguous range of one
-// (b, g)'s visible rows; with at least 128 (b, g) pairs there is one workgroup
+// (b, g)'s visible rows; with at least 256 (b, g) pairs there is one workgroup
 // per pair and the waves merge in LDS, otherwise each pair is split over up to
-// 256 / (B * Hkv) workgroups of at least 128 slots, merged by the last to finish.
+// 256 / (B * Hkv) workgroups of at least 128 slots (so that every compute unit
+// reads), merged by the last to finish.
 constexpr int kDecodeWaves = 8;
 inline int decode_nsplit(const Shape& sh) {
     const long bg = long(sh.B) * sh.Hkv;
-    if (bg >= 128) return 1;
+    if (bg >= 256) return 1;
     const long by_grid = (256 + bg - 1) / bg;
     const long by_rows = (sh.S + 127) / 128;
     const long n = by_grid < by_rows ? by_grid : by_rows;
@@ -173,9 +174,9 @@ inline size_t decode_part_bytes(const Shape& sh) {
                     decode_part_floats(sh.G, sh.D) * 4);
 }
 // Size of the static device array that holds them for lte_decode_step_static;
-// every supported shape needs at most about 3.2 MB (fewer than 128 (b, g) pairs
-// times at most 256 / (B Hkv) + 1 splits, 8320 bytes each).
-constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+// every supported shape needs at most about 4.3 MB (fewer than 256 (b, g) pairs
+// times at most 256 / (B Hkv) + 1 splits: at most 510 partials of 8320 bytes).
+constexpr size_t kStaticScratchBytes = size_t(5) << 20;
 
 struct WsLayout {
     size_t scores, rank, thr, ncand, w1p, select_scratch, dec_part, total;

@@ -61,5 +61,7 @@ def test_static_decode_matches_workspace_decode():
     _run(2, 600, 40, 32, 2, 128, 4, 512, 520, seed=71)
     # then fewer pairs and a smaller cache on the same device: 2 pairs x 3 splits
     _run(1, 300, 40, 8, 2, 128, 4, 200, 100, seed=72)
-    # 128 pairs: one workgroup each, no partials
+    # 128 pairs of 26 slots: one workgroup each, no partials
     _run(32, 64, 12, 8, 4, 64, 2, 16, 8, seed=73)
+    # 128 pairs of 132 slots: 2 splits each, 256 partials
+    _run(32, 150, 12, 16, 4, 128, 4, 64, 64, seed=74)
