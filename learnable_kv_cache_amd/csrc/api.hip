@@ -48,7 +48,6 @@ struct WsPtrs {
     int32_t* rank;
     int32_t* thr;
     int32_t* ncand;
-    uint16_t* w1p;
     uint32_t* select_scratch;
     float* dec_part;
 };
@@ -61,7 +60,6 @@ WsPtrs ws_ptrs(const Shape& sh, int64_t T, void* ws) {
     w.rank = reinterpret_cast<int32_t*>(p + L.rank);
     w.thr = reinterpret_cast<int32_t*>(p + L.thr);
     w.ncand = reinterpret_cast<int32_t*>(p + L.ncand);
-    w.w1p = reinterpret_cast<uint16_t*>(p + L.w1p);
     w.select_scratch = reinterpret_cast<uint32_t*>(p + L.select_scratch);
     w.dec_part = reinterpret_cast<float*>(p + L.dec_part);
     return w;
@@ -181,9 +179,8 @@ int lte_prefill_score(const lte_config* cfg, int64_t T, const uint16_t* k, const
     LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
     WsPtrs w = ws_ptrs(sh, T, workspace);
     hipStream_t st = hipStream_t(stream);
-    LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
     return hip_status(
-        launch_score_prefill(sh, T, nullptr, nullptr, k, v, w.w1p, *cnn, w.scores, st));
+        launch_score_prefill(sh, T, nullptr, nullptr, k, v, *cnn, w.scores, st));
 }
 
 int lte_prefill_select(const lte_config* cfg, int64_t T, const float* score_override,
@@ -266,9 +263,8 @@ int lte_prefill_varlen(const lte_config* cfg, int64_t T, const int32_t* seq_lens
     hipStream_t st = hipStream_t(stream);
     const float* sc = w.scores;
     if (score_override == nullptr) {
-        LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
         LTE_TRY(hip_status(
-            launch_score_prefill(sh, T, seq_lens, nullptr, k, v, w.w1p, *cnn, w.scores, st)));
+            launch_score_prefill(sh, T, seq_lens, nullptr, k, v, *cnn, w.scores, st)));
     } else {
         hipError_t e = hipMemcpyAsync(w.scores, score_override,
                                       size_t(sh.B) * sh.Hkv * T * sizeof(float),
@@ -320,9 +316,8 @@ int lte_prefill_chunk(const lte_config* cfg, int64_t n, const uint16_t* q, const
     const CacheView c = cache_view(sh, cache);
     hipStream_t st = hipStream_t(stream);
     LTE_TRY(hip_status(launch_chunk_gather(sh, int(n), int(E), k, v, c, x, w.scores, ek, ev, st)));
-    LTE_TRY(hip_status(launch_pack_w1(sh, cnn->w1, w.w1p, st)));
     LTE_TRY(hip_status(
-        launch_score_prefill(sh, E, x.ext_len, x.score_lo, ek, ev, w.w1p, *cnn, w.scores, st)));
+        launch_score_prefill(sh, E, x.ext_len, x.score_lo, ek, ev, *cnn, w.scores, st)));
     LTE_TRY(hip_status(
         launch_select(sh, E, x.ext_len, w.scores, w.rank, w.thr, w.ncand, w.select_scratch, st)));
     LTE_TRY(hip_status(launch_attend_prefill(sh, E, x.ext_len, x.q_lo, int(n), q, ek, ev, w.rank,

@@ -179,7 +179,7 @@ inline size_t decode_part_bytes(const Shape& sh) {
 constexpr size_t kStaticScratchBytes = size_t(5) << 20;
 
 struct WsLayout {
-    size_t scores, rank, thr, ncand, w1p, select_scratch, dec_part, total;
+    size_t scores, rank, thr, ncand, select_scratch, dec_part, total;
 };
 
 inline WsLayout ws_layout(const Shape& sh, int64_t T) {
@@ -193,7 +193,6 @@ inline WsLayout ws_layout(const Shape& sh, int64_t T) {
     W.rank = off; off = align256(off + bg * size_t(T) * 4);
     W.thr = off; off = align256(off + bg * size_t(T) * 4);
     W.ncand = off; off = align256(off + bg * 4);
-    W.w1p = off; off = align256(off + size_t(sh.Hkv) * 3 * (2 * sh.D) * kHidden * 2);
     W.select_scratch = off; off = align256(off + (T > 0 ? bg * select_scratch_words(T) * 4 : 0));
     W.total = off;
     return W;
@@ -202,14 +201,12 @@ inline WsLayout ws_layout(const Shape& sh, int64_t T) {
 // ---------------------------------------------------------------------------
 // launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
-hipError_t launch_pack_w1(const Shape& sh, const float* w1, uint16_t* w1p, hipStream_t st);
 // Prefill launchers: T is the row count of every [B][T] tensor; seq_lens (device,
 // [B], or null for T everywhere) gives each sequence's length.
 // score_lo (device, [B][Hkv], or null): rows below it are left as they are.
 hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
                                 const int32_t* score_lo, const uint16_t* k, const uint16_t* v,
-                                const uint16_t* w1p, const lte_cnn& cnn, float* scores,
-                                hipStream_t st);
+                                const lte_cnn& cnn, float* scores, hipStream_t st);
 hipError_t launch_select(const Shape& sh, int64_t T, const int32_t* seq_lens, const float* scores,
                          int32_t* rank, int32_t* thr, int32_t* ncand, uint32_t* scratch,
                          hipStream_t st);

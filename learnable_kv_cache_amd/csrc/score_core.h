@@ -7,9 +7,9 @@
 // token is computable once its receptive field (tokens j-2 .. j+2 for two
 // kernel-3 layers) is present.
 //
-// score_pass: one wave of a prefill workgroup scores 28 tokens, loading its
-// 32 rows' k and v itself, with W1 staged once per workgroup in LDS.
-// score_wave: one wave scores 28 tokens (decode), W1 read from global memory.
+// The prefill scorer (one wave per 28 tokens, W1 staged once per workgroup in
+// LDS) builds on the constants and helpers here; score_wave: one wave scores 28
+// tokens (decode), W1 read from global memory.
 // Layer 1 is written as Y_tap = W1[:, :, tap] . x per token
 // (v_mfma_f32_32x32x16_bf16, 32 tokens x 96 outputs per wave), then
 // h[j] = b1 + Y_0[j-1] + Y_1[j] + Y_2[j+1].
@@ -53,132 +53,12 @@ __device__ __forceinline__ float gelu_erf(float h) {
     return 0.5f * h * (1.0f + erf_as(h * 0.70710678118654752f));
 }
 
-// Packed-W1 entry index x (bf16x8 units) -> (tap, kk, lane); element e of the
-// entry holds W1[o = lane % 32][c = 16 kk + 8 (lane / 32) + e][tap].
-__device__ __forceinline__ void w1p_coords(int x, int KK, int& tap, int& kk, int& lane) {
-    lane = x % 64;
-    kk = (x / 64) % KK;
-    tap = x / (64 * KK);
-}
-
 // x held by lane l ^ 32 (one cross-half swap)
 __device__ __forceinline__ float other_half(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
     // first: every lane's copy of the low half's x; second: of the high half's
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
-
-// Half hf of a lane's layer-1 A operands: k-steps hf*KK/2 .. +KK/2, i.e.
-// channels 16 kk + 8 (lane/32) .. +8 of concat(k, v) of the row at kp, vp
-// (zeros where !ok).
-template <int D>
-__device__ __forceinline__ void score_load_half(bf16x8 (&a)[ScoreSmem<D>::KK / 2],
-                                                const uint16_t* kp, const uint16_t* vp, bool ok,
-                                                int hf) {
-    constexpr int KH = ScoreSmem<D>::KK / 2;
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int q = 0; q < KH; ++q) {
-        const int ch = (hf * KH + q) * 16 + (lane >> 5) * 8;
-        a[q] = ok ? *reinterpret_cast<const bf16x8*>((ch < D) ? (kp + ch) : (vp + (ch - D)))
-                  : bf16x8{};
-    }
-}
-
-// Scores tokens [t0, t0+28) clipped to [tlo, thi] and hands each to store(t, r).
-//   wl       this head's packed W1 in LDS
-//   w2s      this head's W2 [32][3] in LDS
-//   b1o      b1 of output column lane % 32
-//   a0       half 0 of this pass's A operands, loaded by the caller (score_load_half);
-//            on return it holds half 0 of the next pass's, from nkp, nvp (zeros where !nok),
-//            whose loads run under this pass's activation and output-layer work
-//   kp, vp   k and v row of this lane's token (row lane % 32: token t0 - 2 + lane % 32), if ok
-//   act      wave-private LDS tile [kActRows][kActPitch]: hidden activations of rows 1 .. 30
-//   a_zero(x) -> true where layer 2 sees zero padding (outside the sequence)
-// The accumulator element e of lane l holds row 8 (e/4) + 4 (l/32) + e%4 and
-// output column l % 32, so a row's neighbours are in the same lane except
-// across groups of 4 rows, where they sit in lane l ^ 32.
-template <int D, class AZero, class Store>
-__device__ __forceinline__ void score_pass(const bf16x8* wl, const float* w2s, float b1o,
-                                           float b2g, bf16x8 (&a0)[ScoreSmem<D>::KK / 2],
-                                           const uint16_t* kp, const uint16_t* vp, bool ok,
-                                           const uint16_t* nkp, const uint16_t* nvp, bool nok,
-                                           float* act, int t0, int tlo, int thi,
-                                           AZero a_zero, Store store) {
-    constexpr int KK = ScoreSmem<D>::KK;
-    constexpr int KH = KK / 2;                       // k-steps per operand half
-    const int lane = threadIdx.x & 63;
-    const bool hi = (lane & 32) != 0;
-    f32x16 acc[3];
-#pragma unroll
-    for (int tp = 0; tp < 3; ++tp) acc[tp] = f32x16{};
-    // the A operands in two halves of the channels, to keep registers for
-    // four waves per SIMD
-#pragma unroll
-    for (int q = 0; q < KH; ++q) {
-#pragma unroll
-        for (int tp = 0; tp < 3; ++tp) {
-            const bf16x8 bfrag = wl[(tp * KK + q) * 64 + lane];
-            acc[tp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], bfrag, acc[tp], 0, 0, 0);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-        bf16x8 a1[KH];
-        score_load_half<D>(a1, kp, vp, ok, 1);
-#pragma unroll
-        for (int q = 0; q < KH; ++q) {
-#pragma unroll
-            for (int tp = 0; tp < 3; ++tp) {
-                const bf16x8 bfrag = wl[(tp * KK + KH + q) * 64 + lane];
-                acc[tp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], bfrag, acc[tp], 0, 0, 0);
-            }
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    score_load_half<D>(a0, nkp, nvp, nok, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // tap 0 of row-1 and tap 2 of row+1 where they sit in the other lane half
-    float p0[4], p2[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        p0[i] = other_half(acc[0][4 * i + 3]);
-        p2[i] = other_half(acc[2][4 * i]);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int i = e >> 2;
-        const int j = e & 3;
-        const int row = 8 * i + (hi ? 4 : 0) + j;
-        // rows 0 and 31 (the outer halo) take no neighbour: they feed no score
-        const float y0 = (j > 0) ? acc[0][e - 1] : (hi ? p0[i] : (i > 0 ? p0[i - 1] : 0.0f));
-        const float y2 = (j < 3) ? acc[2][e + 1] : (hi ? (i < 3 ? p2[i + 1] : 0.0f) : p2[i]);
-        const float h = b1o + y0 + acc[1][e] + y2;
-        if (row >= 1 && row <= kActRows)
-            act[(row - 1) * kActPitch + (lane & 31)] = a_zero(t0 - 2 + row) ? 0.0f : gelu_erf(h);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // output layer + sigmoid for tokens t0 .. t0+27 (rows 2 .. 29)
-    if (lane < kPassTokens) {
-        const int t = t0 + lane;
-        if (t >= tlo && t <= thi) {
-            float z = b2g;
-            const int r = lane + 1;                          // act row of token t
-#pragma unroll 8
-            for (int o = 0; o < kHidden; ++o) {
-                z += w2s[o * 3 + 0] * act[(r - 1) * kActPitch + o] +
-                     w2s[o * 3 + 1] * act[r * kActPitch + o] +
-                     w2s[o * 3 + 2] * act[(r + 1) * kActPitch + o];
-            }
-            store(t, 1.0f / (1.0f + expf(-z)));
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // One wave scores tokens [t0, t0+28) clipped to [tlo, thi] (the decode
