@@ -195,6 +195,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     scan_g(0);
     share_state();
     __syncthreads();
+    // this chunk's outputs are stored after the next chunk's rows are stashed, so that
+    // the wait for those loads never covers these stores
+    uint16_t opend[16];
     for (int ch = 0; ch < nchunk; ++ch) {
         const int t0 = ch * kChunk;
         const int nrow = min(kChunk, T - t0);
@@ -304,12 +307,10 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
                 ev[e4] = *reinterpret_cast<const float4*>(&Es[tt * 32 + e4 * 8 + half * 4]);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int t = tt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
                 const float e4v[4] = {ev[e >> 2].x, ev[e >> 2].y, ev[e >> 2].z, ev[e >> 2].w};
-                const float o = oi[e] + e4v[e & 3] * ox[e];
-                if (nrow == kChunk || t < nrow)
-                    ob[long(t) * rs] = __builtin_bit_cast(uint16_t, (__bf16)o);
+                opend[e] = __builtin_bit_cast(uint16_t, (__bf16)(oi[e] + e4v[e & 3] * ox[e]));
             }
+            (void)ob;
         }
         // ---- S^T = exp(G_last) S^T + (w K)^T V for this wave's state tiles ------------
         const float decay = __expf(g_last);
@@ -328,6 +329,15 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             stash();
             share_state();
             __syncthreads();
+        }
+        {
+            // element e: row t = xw*32 + (e/4)*8 + h*4 + e%4, dim 32 dw + lane&31
+            uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D + dcol;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = xw * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                if (nrow == kChunk || t < nrow) ob[long(t) * rs] = opend[e];
+            }
         }
     }
     float* so = state_out + long(bh) * D * D;
