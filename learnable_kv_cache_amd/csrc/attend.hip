@@ -15,12 +15,13 @@
 //     tile's first row, via the per-head rank/thr lists), which are listed
 //     while the first band block loads.  Entries that every row of the tile
 //     sees come first, so only the last list blocks need a mask.
-//   * K/V tiles are double-buffered in LDS: the first by direct global->LDS
-//     loads, later ones fetched into registers one block ahead and stored to
-//     the free buffer at the end of the block, so one barrier per block
-//     suffices (with a direct load in flight the compiler would wait for all
-//     outstanding LDS reads before using any).  Scheduling groups keep three
-//     k-steps of K operands and four V operands in flight ahead of the MFMAs.
+//   * K/V tiles are double-buffered in LDS, fetched into registers one block
+//     ahead and stored to the free buffer at the end of the block, so one
+//     barrier per block suffices (with a direct global->LDS load in flight the
+//     compiler would wait for all outstanding LDS reads before using any).  The
+//     first block's fetch is issued behind the rank loads, so the gathered list
+//     is built while it is in flight.  Scheduling groups keep three k-steps of K
+//     operands and four V operands in flight ahead of the MFMAs.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows from LDS are the A
 //     operand, each wave's 32 query rows stay in registers as the B operand.
 //     A lane then owns one query row, so the row max/sum of the online
@@ -155,35 +156,10 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const uint32_t kv_bytes = uint32_t(Hkv * D * 2);
 
     // Blocks: the band blocks first, then the gathered columns below the band.
-    // A tile is filled by direct global->LDS loads: load x of wave wv writes
-    // tile chunks [64x', 64x'+64), x' = wv*LPW + x, lane l chunk 64x'+l; chunk
-    // c is stored chunk c % CPR of tile row c / CPR and holds that key's chunk
-    // (c % CPR) ^ swz(row).
-#define LTE_ISSUE(BLK, KB, VB)                                                              \
-    {                                                                                      \
-        const int fb = (BLK);                                                              \
-        _Pragma("unroll") for (int x = 0; x < LPW; ++x) {                                  \
-            const int xi = wave * LPW + x;                                                 \
-            const int c = xi * 64 + lane;                                                  \
-            const int trow = c / CPR;                                                      \
-            int row;                                                                       \
-            if (fb < nband) row = min(band_lo + fb * 64 + trow, band_hi);                  \
-            else row = int(lst[min((fb - nband) * 64 + trow, kMaxList - 1)] & 0xffffu);    \
-            const uint32_t roff = __umul24(uint32_t(row), kv_bytes);                       \
-            const uint32_t koff = roff + uint32_t(((c % CPR) ^ swz<D>(trow)) * 16);       \
-            const uint32_t voff = roff + uint32_t(((c % CPR) ^ vswz<D>(trow)) * 16);      \
-            __builtin_amdgcn_global_load_lds(                                              \
-                (const __attribute__((address_space(1))) void*)(kbytes + koff),            \
-                (__attribute__((address_space(3))) void*)(&KB[xi * 64]), 16, 0, 0);         \
-            __builtin_amdgcn_global_load_lds(                                              \
-                (const __attribute__((address_space(1))) void*)(vbytes + voff),            \
-                (__attribute__((address_space(3))) void*)(&VB[xi * 64]), 16, 0, 0);         \
-        }                                                                                  \
-    }
-    LTE_ISSUE(0, K0, V0)                          // first band block: needs no list
-    // Blocks after the first are staged through registers instead: with a
-    // direct-to-LDS load outstanding the compiler waits for every LDS read in
-    // flight before using any, which serialises the operand reads of the MFMAs.
+    // Block fb is fetched into registers: load x of wave wv covers tile chunks
+    // [64x', 64x'+64), x' = wv*LPW + x, lane l chunk 64x'+l; chunk c is stored as
+    // chunk c % CPR of tile row c / CPR and holds that key's chunk (c % CPR) ^
+    // swz(row) (K) or ^ vswz(row) (V).
     u32x4 kst[LPW], vst[LPW];
 #define LTE_FETCH(BLK)                                                                      \
     {                                                                                      \
@@ -249,6 +225,9 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     // list entry e is visible to this row iff e <= lim (field <= thr_row + 1)
     const uint32_t lim = (uint32_t(min(max(thr_row + 1, 0), 0xfffe)) << 16) | 0xffffu;
     const float csc = kLog2e * rsqrtf(float(D));
+    // the first band block (needs no list), fetched behind the rank loads so that the
+    // list is built while it is in flight
+    LTE_FETCH(0)
 
     if (tid < kBr) brank[tid] = brv;
     // ---- gathered columns below the band: the sink, then the candidates alive at the
@@ -336,8 +315,8 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x16{};
 
-    __builtin_amdgcn_s_waitcnt(0);                // this wave's loads of block 0 landed
-    __syncthreads();                              // everyone's, and lfull, brank
+    LTE_STORE(K0, V0)
+    __syncthreads();                              // block 0, lfull, brank
 
     uint32_t vrd[DT];           // this lane's byte offsets of its V operand pieces
     {
@@ -543,7 +522,6 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         step(blk, K0, V0, K1, V1);
         if (blk + 1 < nblk) step(blk + 1, K1, V1, K0, V0);
     }
-#undef LTE_ISSUE
 #undef LTE_FETCH
 #undef LTE_STORE
 
