@@ -187,6 +187,36 @@ def test_repeat_runs_are_bitwise_identical():
         assert np.array_equal(va[n], vb[n]), n
 
 
+def test_repeat_runs_are_bitwise_identical_full_size():
+    """The bench layer (B32 T4096 Hq16 Hkv4 D128 s4 w512 C512, CNN) prefilled twice into
+    fresh zeroed caches: outputs, every workspace view and the caches agree bit for bit.
+    Every kernel's work split is static and no result depends on timing."""
+    inp = synth.workload_inputs(3)
+    wl = inp["workload"]
+    T = inp["T"]
+    q, k, v = (_dev(x) for x in (inp["q"], inp["k"], inp["v"]))
+    layer = lte.Layer(lte.Config(wl.B, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window, wl.capacity))
+    cnn = lte.CNN(inp["cnn"])
+    runs = []
+    for _ in range(2):
+        ws = layer.alloc_workspace(T)
+        cache = torch.zeros(layer.cache_bytes(), dtype=torch.uint8, device="cuda")
+        layer.cache_init(cache)
+        out = layer.prefill(q, k, v, cnn=cnn, cache=cache, workspace=ws)
+        torch.cuda.synchronize()
+        views = {n: x.clone() for n, x in layer.workspace_views(ws, T).items()}
+        runs.append((out.clone(), views, cache))
+        del ws
+    (oa, va, ca), (ob, vb, cb) = runs
+    assert torch.equal(oa, ob)
+    for n in va:
+        if va[n].is_floating_point():
+            assert torch.equal(torch.nan_to_num(va[n], nan=-7.0), torch.nan_to_num(vb[n], nan=-7.0)), n
+        else:
+            assert torch.equal(va[n], vb[n]), n
+    assert torch.equal(ca, cb)
+
+
 def test_attend_beside_cache_build_matches_serial_prefill():
     """After select, attend and the cache build share only read-only inputs: run on two
     streams at once they give the serial prefill's output and cache bit for bit."""
