@@ -12,9 +12,10 @@
 //     Its band of keys is [i0-w+1, i0+P-1] (P+w-1 keys for P rows).
 //   * keys are processed in blocks of 64: first the band blocks, then the
 //     gathered columns below the band (sink + retained tokens alive at the
-//     tile's first row, via the per-head rank/thr lists), which are listed
-//     while the first band block loads.  Entries that every row of the tile
-//     sees come first, so only the last list blocks need a mask.
+//     tile's first row, via the per-head rank/thr lists).  With two band
+//     blocks or more the list is built after the first one, whose compute
+//     hides the rank loads' latency.  Entries that every row of the tile sees
+//     come first, so only the last list blocks need a mask.
 //   * K/V tiles are double-buffered in LDS, fetched into registers one block
 //     ahead and stored to the free buffer at the end of the block, so one
 //     barrier per block suffices (with a direct global->LDS load in flight the
@@ -237,6 +238,9 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     //      Ballot compaction (order by pass slot u, then wave, then lane); transient
     //      entries are collected downward from the top of lst and moved after the
     //      stable ones at the end -------------------------------------------------------
+    int nblk = nband;                             // the list's blocks join once it is built
+    bool listed = false;
+    auto build_list = [&]() {
     int len = ns;                                 // sink + stable entries so far
     int ntr = 0;                                  // transient entries so far
     for (int j = tid; j < ns; j += NT) lst[j] = uint32_t(j);           // field 0: always visible
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     // pad to whole blocks with entries no row sees (field 0xffff, key 0)
     for (int e = len + tid; e < ((len + 63) & ~63); e += NT) lst[e] = 0xffff0000u;
     const int nlist = (len + 63) / 64;
-    const int nblk = nband + nlist;
+    nblk = nband + nlist;
     __syncthreads();                              // list complete
     // thr is non-increasing, so the tile's last row has the strictest list
     // threshold: a block whose entries all pass it needs no mask
@@ -309,6 +313,12 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         }
     }
 
+        listed = true;
+    };
+    // with two band blocks or more the list is built after the first block, whose
+    // compute hides the rank loads' latency; block 1 is then a band block
+    if (nband < 2) build_list();
+
     float m_run = -INFINITY;
     float l_run = 0.0f;
     f32x16 acc_o[DT];
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x16{};
 
     LTE_STORE(K0, V0)
-    __syncthreads();                              // block 0, lfull, brank
+    __syncthreads();                              // block 0, brank (and lfull when listed)
 
     uint32_t vrd[DT];           // this lane's byte offsets of its V operand pieces
     {
@@ -518,9 +528,11 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         if (blk + 1 < nblk) LTE_STORE(KN, VN)     // the other buffers: free since the last barrier
         __syncthreads();                          // everyone's stores; and the current tiles are free
     };
-    for (int blk = 0; blk < nblk; blk += 2) {
-        step(blk, K0, V0, K1, V1);
-        if (blk + 1 < nblk) step(blk + 1, K1, V1, K0, V0);
+    step(0, K0, V0, K1, V1);
+    if (!listed) build_list();
+    for (int blk = 1; blk < nblk; blk += 2) {
+        step(blk, K1, V1, K0, V0);
+        if (blk + 1 < nblk) step(blk + 1, K0, V0, K1, V1);
     }
 #undef LTE_FETCH
 #undef LTE_STORE
