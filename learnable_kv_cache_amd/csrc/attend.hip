@@ -16,13 +16,15 @@
 //     blocks or more the list is built after the first one, whose compute
 //     hides the rank loads' latency.  Entries that every row of the tile sees
 //     come first, so only the last list blocks need a mask.
-//   * K/V tiles are double-buffered in LDS, fetched into registers one block
-//     ahead and stored to the free buffer at the end of the block, so one
-//     barrier per block suffices (with a direct global->LDS load in flight the
-//     compiler would wait for all outstanding LDS reads before using any).  The
-//     first block's fetch is issued behind the rank loads, so the gathered list
-//     is built while it is in flight.  Scheduling groups keep three k-steps of K
-//     operands and four V operands in flight ahead of the MFMAs.
+//   * K/V tiles are double-buffered in LDS.  The next block is copied straight
+//     from global memory into the free buffer while the current one is
+//     computed (global_load_lds, issued from inline assembly so that the
+//     compiler does not make the current buffer's operand reads wait for it);
+//     each wave waits for its own copies at the end of the block, and one
+//     barrier per block publishes them.  The first block's copy is issued
+//     behind the rank loads, so the gathered list is built while it is in
+//     flight.  Scheduling groups keep three k-steps of K operands and four V
+//     operands in flight ahead of the MFMAs.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows from LDS are the A
 //     operand, each wave's 32 query rows stay in registers as the B operand.
 //     A lane then owns one query row, so the row max/sum of the online
@@ -42,6 +44,8 @@
 //     passes 2^8; the running output is rarely rescaled.
 //   * the output is staged through LDS and stored as whole rows.
 #include "lte_internal.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 on the clobber list of the tile copies
 
 namespace lte {
 namespace {
@@ -125,6 +129,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int half = lane >> 5;          // which half of the MFMA k-dimension a lane holds
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so map
     // each XCD's share to a contiguous run of tiles (neighbouring tiles of a
@@ -157,12 +162,15 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const uint32_t kv_bytes = uint32_t(Hkv * D * 2);
 
     // Blocks: the band blocks first, then the gathered columns below the band.
-    // Block fb is fetched into registers: load x of wave wv covers tile chunks
-    // [64x', 64x'+64), x' = wv*LPW + x, lane l chunk 64x'+l; chunk c is stored as
-    // chunk c % CPR of tile row c / CPR and holds that key's chunk (c % CPR) ^
-    // swz(row) (K) or ^ vswz(row) (V).
-    u32x4 kst[LPW], vst[LPW];
-#define LTE_FETCH(BLK)                                                                      \
+    // Block fb is copied straight from global memory into the tile buffers KB, VB:
+    // load x of wave wv covers tile chunks [64x', 64x'+64), x' = wv*LPW + x, lane l
+    // chunk 64x'+l; chunk c is tile row c / CPR at position c % CPR and holds that
+    // key's chunk (c % CPR) ^ swz(row) (K) or ^ vswz(row) (V).  The copies are
+    // global_load_lds written as inline assembly: the compiler, which cannot tell
+    // their LDS writes from the operand reads of the other buffer, would otherwise
+    // make every LDS read wait for them.  The end of each block waits for them
+    // (LTE_WAIT_COPIES).  The kernel sets M0 only here.
+#define LTE_COPY(BLK, KB, VB)                                                               \
     {                                                                                      \
         const int fb = (BLK);                                                              \
         _Pragma("unroll") for (int x = 0; x < LPW; ++x) {                                  \
@@ -172,19 +180,19 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
             if (fb < nband) row = min(band_lo + fb * 64 + trow, band_hi);                  \
             else row = int(lst[min((fb - nband) * 64 + trow, kMaxList - 1)] & 0xffffu);    \
             const uint32_t roff = __umul24(uint32_t(row), kv_bytes);                       \
-            kst[x] = *reinterpret_cast<const u32x4*>(                                      \
-                kbytes + roff + uint32_t(((c % CPR) ^ swz<D>(trow)) * 16));                \
-            vst[x] = *reinterpret_cast<const u32x4*>(                                      \
-                vbytes + roff + uint32_t(((c % CPR) ^ vswz<D>(trow)) * 16));               \
+            const char* ks_ = kbytes + roff + uint32_t(((c % CPR) ^ swz<D>(trow)) * 16);   \
+            const char* vs_ = vbytes + roff + uint32_t(((c % CPR) ^ vswz<D>(trow)) * 16);  \
+            const uint32_t kl_ = uint32_t(reinterpret_cast<uintptr_t>(                     \
+                (__attribute__((address_space(3))) void*)(&KB[(wave_u * LPW + x) * 64]))); \
+            const uint32_t vl_ = uint32_t(reinterpret_cast<uintptr_t>(                     \
+                (__attribute__((address_space(3))) void*)(&VB[(wave_u * LPW + x) * 64]))); \
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"    \
+                         :: "v"(ks_), "s"(kl_) : "memory", "m0");                           \
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"    \
+                         :: "v"(vs_), "s"(vl_) : "memory", "m0");                           \
         }                                                                                  \
     }
-#define LTE_STORE(KB, VB)                                                                   \
-    {                                                                                      \
-        _Pragma("unroll") for (int x = 0; x < LPW; ++x) {                                  \
-            KB[(wave * LPW + x) * 64 + lane] = kst[x];                                     \
-            VB[(wave * LPW + x) * 64 + lane] = vst[x];                                     \
-        }                                                                                  \
-    }
+#define LTE_WAIT_COPIES() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
     // ---- prologue: every global load first, then the LDS work ----------------------
     constexpr int NT = NW * 64;
@@ -226,9 +234,9 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     // list entry e is visible to this row iff e <= lim (field <= thr_row + 1)
     const uint32_t lim = (uint32_t(min(max(thr_row + 1, 0), 0xfffe)) << 16) | 0xffffu;
     const float csc = kLog2e * rsqrtf(float(D));
-    // the first band block (needs no list), fetched behind the rank loads so that the
+    // the first band block (needs no list), copied behind the rank loads so that the
     // list is built while it is in flight
-    LTE_FETCH(0)
+    LTE_COPY(0, K0, V0)
 
     if (tid < kBr) brank[tid] = brv;
     // ---- gathered columns below the band: the sink, then the candidates alive at the
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x16{};
 
-    LTE_STORE(K0, V0)
+    LTE_WAIT_COPIES();
     __syncthreads();                              // block 0, brank (and lfull when listed)
 
     uint32_t vrd[DT];           // this lane's byte offsets of its V operand pieces
@@ -339,9 +347,9 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
             vrd[dt] = uint32_t(key0 * CPR * 16 + ((4 * dt + c_lo) ^ vswz<D>(key0)) * 16 + 8 * (i & 1));
     }
 
-    // one block: issue the next block's loads into (KN, VN), compute on (KC, VC)
+    // one block: copy the next block into (KN, VN), compute on (KC, VC)
     auto step = [&](const int blk, u32x4* KC, u32x4* VC, u32x4* KN, u32x4* VN) {
-        if (blk + 1 < nblk) LTE_FETCH(blk + 1)             // in flight during this block
+        if (blk + 1 < nblk) LTE_COPY(blk + 1, KN, VN)      // in flight during this block
         const bool is_list = blk >= nband;
         const int lb = blk - nband;                        // list block index
         const int jb0 = band_lo + blk * 64;                // first key of a band block
@@ -525,8 +533,8 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
-        if (blk + 1 < nblk) LTE_STORE(KN, VN)     // the other buffers: free since the last barrier
-        __syncthreads();                          // everyone's stores; and the current tiles are free
+        LTE_WAIT_COPIES();                        // this wave's copies of the next block
+        __syncthreads();                          // everyone's copies; and the current tiles are free
     };
     step(0, K0, V0, K1, V1);
     if (!listed) build_list();
@@ -534,8 +542,8 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         step(blk, K1, V1, K0, V0);
         if (blk + 1 < nblk) step(blk + 1, K0, V0, K1, V1);
     }
-#undef LTE_FETCH
-#undef LTE_STORE
+#undef LTE_COPY
+#undef LTE_WAIT_COPIES
 
     // ---- normalise, stage the wave's 32 rows as bf16 in LDS (the K/V tiles are free
     //      after the last block's barrier), then store whole rows: the G heads of one
