@@ -133,10 +133,12 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so map
     // each XCD's share to a contiguous run of tiles (neighbouring tiles of a
-    // head share most of their band keys in that XCD's L2).
+    // head share most of their band keys in that XCD's L2).  Each run is taken
+    // from its end: a head's later tiles carry the longer gathered lists, so the
+    // cheapest tiles come last and the launch's tail is short.
     const int ngrid = gridDim.x;
-    int lin = blockIdx.x;
-    if ((ngrid & 7) == 0) lin = (blockIdx.x & 7) * (ngrid >> 3) + (blockIdx.x >> 3);
+    int lin = ngrid - 1 - blockIdx.x;
+    if ((ngrid & 7) == 0) lin = (blockIdx.x & 7) * (ngrid >> 3) + ((ngrid >> 3) - 1 - (blockIdx.x >> 3));
     const int bg = lin / ntile;
     const int tile = lin % ntile;
     const int b = bg / Hkv;
