@@ -36,6 +36,10 @@
 //   * K and V tiles sit in LDS as 16-byte chunks XOR-swizzled by row (each
 //     tensor its own pattern), so the row-strided MFMA operand reads hit
 //     distinct banks.
+//   * A block that needs a mask gets it as the first k-step's accumulator (0,
+//     or -inf for a hidden key), built before its MFMAs: the logits then leave
+//     the MFMAs in the registers the softmax reads, where a mask applied
+//     afterwards made the compiler move all 32 of them on every unmasked block.
 //   * fp32 online softmax on raw logits, the 1/sqrt(D) scale and log2(e)
 //     folded into one FMA before exp2; masked keys are -inf.  p is taken
 //     against a lazy reference maximum: a lane's sum of its block's p bounds
@@ -356,12 +360,82 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         const int lb = blk - nband;                        // list block index
         const int jb0 = band_lo + blk * 64;                // first key of a band block
 
-        // ---- S^T = K Q^T for 64 keys x this wave's 32 rows -----------------------
+        // ---- S^T = K Q^T for 64 keys x this wave's 32 rows.  Hidden keys enter as
+        //      -inf through the first k-step's accumulator, built (only for blocks that
+        //      need a mask) before the MFMAs; element e of subtile ks is key slot
+        //      ks*32 + (e/4)*8 + half*4 + e%4 of this block --------------------------------
+        const bool list_full =
+            is_list && __builtin_amdgcn_readfirstlane(lfull[min(lb, kMaxList / 64 - 1)]);
+        // d = irow - j: visible iff 0 <= d < w, or d >= w and j passes (sink ranks read
+        // -1); band blocks past kBr keys hold no d >= w
+        const bool causal_ok = jb0 + 63 <= i0;               // d >= 0 on every row
+        const bool in_window = jb0 >= i_last - w + 1;        // d < w on every row
+        const bool masked = is_list ? !list_full : !(causal_ok && in_window);
         f32x16 sacc[2];
-        sacc[0] = f32x16{};
-        sacc[1] = f32x16{};
+        {
+            bf16x8 a0[2];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+            for (int ks = 0; ks < 2; ++ks) {
+                const int row = ks * 32 + (lane & 31);
+                a0[ks] = __builtin_bit_cast(bf16x8, KC[row * CPR + (half ^ swz<D>(row))]);
+            }
+            if (masked) {
+                f32x16 bias[2];
+                bias[0] = f32x16{};
+                bias[1] = f32x16{};
+                if (is_list) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            const int t0 = ks * 32 + e4 * 8 + half * 4;
+                            const u32x4 ent = *reinterpret_cast<const u32x4*>(&lst[lb * 64 + t0]);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (!(ent[u] <= lim)) bias[ks][e4 * 4 + u] = -INFINITY;
+                        }
+                    }
+                } else {
+                    const int dbase = irow - jb0 - half * 4;
+                    if (in_window) {                         // the causal edge only
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) {
+                                const int d = dbase - (ks * 32 + (e >> 2) * 8 + (e & 3));
+                                if (d < 0) bias[ks][e] = -INFINITY;
+                            }
+                    } else {                                 // the window edge, maybe both
+                        const int rb = min(blk, kBr / 64 - 1) * 64;
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                            for (int e4 = 0; e4 < 4; ++e4) {
+                                const int t0 = ks * 32 + e4 * 8 + half * 4;
+                                const int4 br = *reinterpret_cast<const int4*>(&brank[rb + t0]);
+                                const int bv[4] = {br.x, br.y, br.z, br.w};
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) {
+                                    const int d = dbase - (ks * 32 + e4 * 8 + u);
+                                    const bool vis = (unsigned(d) < unsigned(w)) |
+                                                     ((d >= 0) & (bv[u] <= thr_row));
+                                    if (!vis) bias[ks][e4 * 4 + u] = -INFINITY;
+                                }
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    sacc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks], qf[0], bias[ks], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    sacc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks], qf[0], f32x16{}, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int kk = 1; kk < KK; ++kk) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int row = ks * 32 + (lane & 31);
@@ -372,79 +446,13 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         }
         // schedule: the K operands of the next three k-steps are in flight while
         // this one's MFMAs run
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
         for (int x = 0; x < KK - 3; ++x) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
-        // ---- mask in place: element e of subtile ks is key slot
-        //      ks*32 + (e/4)*8 + half*4 + e%4 of this block ----------------------------
-        const bool list_full =
-            is_list && __builtin_amdgcn_readfirstlane(lfull[min(lb, kMaxList / 64 - 1)]);
-        if (is_list && !list_full) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int t0 = ks * 32 + e4 * 8 + half * 4;
-                    const u32x4 ent = *reinterpret_cast<const u32x4*>(&lst[lb * 64 + t0]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (!(ent[u] <= lim)) sacc[ks][e4 * 4 + u] = -INFINITY;
-                }
-            }
-        } else if (!is_list) {
-            // d = irow - j: visible iff 0 <= d < w, or d >= w and j passes (sink
-            // ranks read -1); band blocks past kBr keys hold no d >= w
-            const bool causal_ok = jb0 + 63 <= i0;           // d >= 0 on every row
-            const bool in_window = jb0 >= i_last - w + 1;    // d < w on every row
-            const int dbase = irow - jb0 - half * 4;
-            if (causal_ok && !in_window) {
-                const int rb = min(blk, kBr / 64 - 1) * 64;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                    for (int e4 = 0; e4 < 4; ++e4) {
-                        const int t0 = ks * 32 + e4 * 8 + half * 4;
-                        const int4 br = *reinterpret_cast<const int4*>(&brank[rb + t0]);
-                        const int bv[4] = {br.x, br.y, br.z, br.w};
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int d = dbase - (ks * 32 + e4 * 8 + u);
-                            if (!((d < w) | (bv[u] <= thr_row))) sacc[ks][e4 * 4 + u] = -INFINITY;
-                        }
-                    }
-                }
-            } else if (in_window && !causal_ok) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int d = dbase - (ks * 32 + (e >> 2) * 8 + (e & 3));
-                        if (d < 0) sacc[ks][e] = -INFINITY;
-                    }
-            } else if (!in_window) {
-                const int rb = min(blk, kBr / 64 - 1) * 64;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                    for (int e4 = 0; e4 < 4; ++e4) {
-                        const int t0 = ks * 32 + e4 * 8 + half * 4;
-                        const int4 br = *reinterpret_cast<const int4*>(&brank[rb + t0]);
-                        const int bv[4] = {br.x, br.y, br.z, br.w};
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int d = dbase - (ks * 32 + e4 * 8 + u);
-                            const bool vis = (unsigned(d) < unsigned(w)) |
-                                             ((d >= 0) & (bv[u] <= thr_row));
-                            if (!vis) sacc[ks][e4 * 4 + u] = -INFINITY;
-                        }
-                    }
-                }
-            }
-        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
 
         // ---- online softmax in raw logits, scale folded into the exponent; row =
         //      this lane's query, keys split with lane^32.  p is taken against the
