@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     constexpr int TCH = 64 * CPR;           // chunks of one 64-key tile
     constexpr int LPW = TCH / 64 / NW;      // direct loads per wave per tile and tensor
     constexpr int kMaxList = kMaxSink + kMaxCapacity + P;    // sink, retained, transient room
-    constexpr int kListTop = kMaxList - 1;
+    constexpr int kListTop = kMaxList + 63;       // transient entries gather below it
     constexpr int kBr = P > 64 ? P : 64;    // band keys whose rank can matter, rounded up
     static_assert(LPW >= 1 && LPW * 64 * NW == TCH, "tile split");
 
@@ -124,11 +124,10 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     __shared__ __align__(16) u32x4 V1[TCH];
     // (field << 16) | token index; field = rank + 1 of a retained token, 0 for
     // a sink token, 0xffff for padding
-    __shared__ __align__(16) uint32_t lst[kMaxList];
+    __shared__ __align__(16) uint32_t lst[kMaxList + 64];
     __shared__ __align__(16) int32_t brank[kBr];
     __shared__ int lfull[kMaxList / 64];            // list block visible to every row of the tile
-    __shared__ int wcnt[128];                       // per (pass slot, wave) counts: stable, transient
-    __shared__ int woff[130];                       // their exclusive prefixes, then the totals
+    __shared__ int wcnt[2][64];                     // per (pass slot, wave) counts, stable | transient << 16
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -257,6 +256,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     auto build_list = [&]() {
     int len = ns;                                 // sink + stable entries so far
     int ntr = 0;                                  // transient entries so far
+    int par = 0;                                  // count buffer of this pass
     for (int j = tid; j < ns; j += NT) lst[j] = uint32_t(j);           // field 0: always visible
     for (int base = s; base < band_lo; base += LU * NT) {
         if (base != s) {
@@ -276,42 +276,40 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
             const unsigned long long m = st ? ms : mt;
             pre[u] = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
                                                __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-            if (lane == 0) {
-                wcnt[u * NW + wave] = __popcll(ms);
-                wcnt[64 + u * NW + wave] = __popcll(mt);
-            }
+            if (lane == 0) wcnt[par][u * NW + wave] = __popcll(ms) | (__popcll(mt) << 16);
         }
-        __syncthreads();
-        if (wave < 2) {                           // exclusive scans of the 64 + 64 counts
-            const int c = wcnt[wave * 64 + lane];
-            int incl = c;
+        __syncthreads();                          // the pass's counts
+        // every wave scans the 64 packed counts itself (each total < 2^13), so no
+        // second barrier; the counts alternate between two buffers, so the next
+        // pass's writes wait only for its own barrier
+        const int c = wcnt[par][lane];
+        int incl = c;
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int y = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += y;
-            }
-            woff[wave * 65 + lane] = incl - c;
-            if (lane == 63) woff[wave * 65 + 64] = incl;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += y;
         }
-        __syncthreads();
+        const int excl = incl - c;
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
 #pragma unroll
         for (int u = 0; u < LU; ++u) {
+            const int off = __builtin_amdgcn_readlane(excl, u * NW + wave);
             const uint32_t ent = (uint32_t(rr[u] + 1) << 16) | uint32_t(base + u * NT + tid);
             if (rr[u] <= thr_last)
-                lst[len + woff[u * NW + wave] + int(pre[u])] = ent;
+                lst[len + (off & 0xffff) + int(pre[u])] = ent;
             else if (rr[u] <= thr0)
-                lst[kListTop - (ntr + woff[65 + u * NW + wave] + int(pre[u]))] = ent;
+                lst[kListTop - (ntr + (off >> 16) + int(pre[u]))] = ent;
         }
-        len += woff[64];
-        ntr += woff[65 + 64];
-        __syncthreads();                          // wcnt and woff are reused
+        len += tot & 0xffff;
+        ntr += tot >> 16;
+        par ^= 1;
     }
-    // transient entries after the stable ones (the regions do not overlap: len + ntr <=
-    // s + C and ntr < P, while lst holds s + C + P entries)
+    __syncthreads();                              // every entry placed
+    // transient entries after the stable ones, and the padding to whole blocks with
+    // entries no row sees (field 0xffff, key 0), in one pass: the transient entries sit
+    // at or above kMaxList + 64 - P, past both (len + ntr <= s + C and ntr < P)
     for (int e = tid; e < ntr; e += NT) lst[len + e] = lst[kListTop - e];
     len += ntr;
-    __syncthreads();
-    // pad to whole blocks with entries no row sees (field 0xffff, key 0)
     for (int e = len + tid; e < ((len + 63) & ~63); e += NT) lst[e] = 0xffff0000u;
     const int nlist = (len + 63) / 64;
     nblk = nband + nlist;
