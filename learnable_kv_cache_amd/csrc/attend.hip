@@ -199,6 +199,20 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     }
 #define LTE_WAIT_COPIES() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
+    // ---- this lane's query row (its loads first: they come from HBM) ---------------
+    const int rtile = wave * 32 + (lane & 31);
+    const int p_row = rtile / G;
+    const int hh = rtile % G;
+    const int i_row = i0 + p_row;
+    const int irow = i_row <= i_last ? i_row : i_last;
+    const int h = g * G + hh;
+    bf16x8 qf[KK];
+    {
+        const uint16_t* qrow = q + ((long(b) * qrows + max(irow - qlo, 0)) * Hq + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + half * 8);
+    }
     // ---- prologue: every global load first, then the LDS work ----------------------
     constexpr int NT = NW * 64;
     constexpr int LU = 8;                         // list candidates per thread and pass
@@ -221,20 +235,6 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         rr[u] = (j < band_lo) ? rk[j] : kNotCand;
     }
 
-    // ---- this lane's query row --------------------------------------------------
-    const int rtile = wave * 32 + (lane & 31);
-    const int p_row = rtile / G;
-    const int hh = rtile % G;
-    const int i_row = i0 + p_row;
-    const int irow = i_row <= i_last ? i_row : i_last;
-    const int h = g * G + hh;
-    bf16x8 qf[KK];
-    {
-        const uint16_t* qrow = q + ((long(b) * qrows + max(irow - qlo, 0)) * Hq + h) * D;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + half * 8);
-    }
     const int thr_row = (irow - w >= 0) ? th[irow - w] : -2;
     // list entry e is visible to this row iff e <= lim (field <= thr_row + 1)
     const uint32_t lim = (uint32_t(min(max(thr_row + 1, 0), 0xfffe)) << 16) | 0xffffu;
