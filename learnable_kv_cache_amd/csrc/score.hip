@@ -11,7 +11,8 @@
 // 96-term second layer and the sigmoid run in fp32.
 //
 // Grid: about one workgroup of 8 waves per CU, a few per (batch, KV head),
-// each over a contiguous run of 224-token chunks (8 waves x 28 tokens), with
+// each over an even share of the head's tokens in 224-token chunks (8 waves x
+// 28 tokens), with
 // the head's W1 converted to bf16 and staged in LDS once.  Every wave holds the
 // next pass's rows in registers while it computes the current one.  Tokens outside [0, T_b) read as zero (first layer's
 // padding) and their hidden activations are zero (second layer's padding);
@@ -114,15 +115,15 @@ __device__ __forceinline__ void score_load_row(bf16x8 (&a)[ScoreSmem<D>::KK], co
     }
 }
 
-// One workgroup (8 waves, one per SIMD pair) per compute unit scores a contiguous
-// run of 224-token chunks of one (batch, KV head): each wave takes 28 tokens of a
+// One workgroup (8 waves, one per SIMD pair) per compute unit scores an even share
+// of one (batch, KV head)'s tokens in 224-token chunks: each wave takes 28 tokens of a
 // chunk per pass.  A pass's rows are loaded during the pass before it, into the
 // second of two register sets, so every wave keeps a whole pass of loads in flight
 // while it computes; the score of a pass is stored at the start of the next one,
 // after its wait, so that the wait never covers a store.
 template <int D>
 __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_eu(2))) void score_prefill_kernel(
-    int T, int Hkv, int nchunk, int nsplit, const int32_t* __restrict__ seq_lens,
+    int T, int Hkv, int nsplit, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ score_lo, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v,
     const float* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
@@ -142,11 +143,14 @@ __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_e
     const int g = bg % Hkv;
     const int Tb = seq_len_of(seq_lens, b, T);
     const int lo = score_lo ? score_lo[bg] : 0;              // rows below keep their scores
-    // this workgroup's chunks, without those wholly past T_b or below lo
-    const int per = (nchunk + nsplit - 1) / nsplit;
-    const int c_begin = max(part * per, lo / kChunkTokens);
-    const int c_end = min(min(nchunk, (part + 1) * per), (Tb + kChunkTokens - 1) / kChunkTokens);
-    if (c_begin >= c_end) return;
+    // this workgroup's tokens: an even share of the head's T rows, without those past
+    // T_b or below lo, in 224-token chunks from its first token
+    const int per = (T + nsplit - 1) / nsplit;
+    const int t_begin = max(part * per, lo);
+    const int t_end = min((part + 1) * per, Tb);
+    if (t_begin >= t_end) return;
+    const int c_begin = 0;
+    const int c_end = (t_end - t_begin + kChunkTokens - 1) / kChunkTokens;
 
     const long row_stride = long(Hkv) * D;
     const uint16_t* kb = k + (long(b) * T * Hkv + g) * D;
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_e
     // this lane's row of chunk c: token c * 224 + wave * 28 - 2 + lane % 32
     const int tok0 = wave * kPassTokens - 2 + (lane & 31);
     auto load = [&](bf16x8 (&a)[KK], int c) {
-        const int tok = c * kChunkTokens + tok0;
+        const int tok = t_begin + c * kChunkTokens + tok0;
         score_load_row<D>(a, kb + long(tok) * row_stride, vb + long(tok) * row_stride,
                           tok >= 0 && tok < Tb);
     };
@@ -207,18 +211,18 @@ __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_e
     auto pass = [&](int c, const bf16x8 (&a)[KK], bf16x8 (&an)[KK]) {
         __builtin_amdgcn_s_waitcnt(0);                       // a has landed
         __builtin_amdgcn_sched_barrier(0);
-        if (pend && pt >= lo) out[pt] = pr;
+        if (pend) out[pt] = pr;
         if (c + 1 < c_end) load(an, c + 1);
         __builtin_amdgcn_sched_barrier(0);
-        pend = score_rows<D>(wl, w2s, b1o, b2g, a, my_act, c * kChunkTokens + wave * kPassTokens,
-                             0, Tb - 1, [&](int x) { return x < 0 || x >= Tb; }, pt, pr);
+        pend = score_rows<D>(wl, w2s, b1o, b2g, a, my_act, t_begin + c * kChunkTokens + wave * kPassTokens,
+                             t_begin, t_end - 1, [&](int x) { return x < 0 || x >= Tb; }, pt, pr);
     };
     for (int c = c_begin; c < c_end; c += 2) {
         pass(c, aA, aB);
         if (c + 1 >= c_end) break;
         pass(c + 1, aB, aA);
     }
-    if (pend && pt >= lo) out[pt] = pr;
+    if (pend) out[pt] = pr;
 }
 
 }  // namespace
@@ -227,7 +231,7 @@ hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_l
                                 const int32_t* score_lo, const uint16_t* k, const uint16_t* v,
                                 const lte_cnn& cnn, float* scores, hipStream_t st) {
     // about one workgroup per CU over the whole grid (256 CUs), each (b, g)
-    // split into nsplit runs of chunks
+    // split into nsplit even token ranges
     const int nchunk = int((T + kChunkTokens - 1) / kChunkTokens);
     const long bgs = long(sh.B) * sh.Hkv;
     long nsplit = (256 + bgs - 1) / bgs;
@@ -236,11 +240,11 @@ hipError_t launch_score_prefill(const Shape& sh, int64_t T, const int32_t* seq_l
     dim3 grid(unsigned(bgs * nsplit));
     if (sh.D == 128) {
         hipLaunchKernelGGL(score_prefill_kernel<128>, grid, dim3(64 * kScoreWaves), 0, st, int(T), sh.Hkv,
-                           nchunk, int(nsplit), seq_lens, score_lo, k, v, cnn.w1, cnn.b1, cnn.w2,
+                           int(nsplit), seq_lens, score_lo, k, v, cnn.w1, cnn.b1, cnn.w2,
                            cnn.b2, scores);
     } else {
         hipLaunchKernelGGL(score_prefill_kernel<64>, grid, dim3(64 * kScoreWaves), 0, st, int(T), sh.Hkv,
-                           nchunk, int(nsplit), seq_lens, score_lo, k, v, cnn.w1, cnn.b1, cnn.w2,
+                           int(nsplit), seq_lens, score_lo, k, v, cnn.w1, cnn.b1, cnn.w2,
                            cnn.b2, scores);
     }
     return hipGetLastError();
