@@ -442,15 +442,15 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
                 sacc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[ks], 0, 0, 0);
             }
         }
-        // schedule: the K operands of the next three k-steps are in flight while
-        // this one's MFMAs run
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        // schedule (k-steps 1 .. KK-1): the K operands of the next three k-steps are
+        // in flight while this one's MFMAs run
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
 #pragma unroll
-        for (int x = 0; x < KK - 3; ++x) {
+        for (int x = 0; x < KK - 4; ++x) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
 
         // ---- online softmax in raw logits, scale folded into the exponent; row =
         //      this lane's query, keys split with lane^32.  p is taken against the
