@@ -159,8 +159,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) __attribute__((amdgpu_waves_per_e
     const int tok0 = wave * kPassTokens - 2 + (lane & 31);
     auto load = [&](bf16x8 (&a)[KK], int c) {
         const int tok = t_begin + c * kChunkTokens + tok0;
+        // rows past t_end + 1 feed no score of this range: read as zero, no traffic
         score_load_row<D>(a, kb + long(tok) * row_stride, vb + long(tok) * row_stride,
-                          tok >= 0 && tok < Tb);
+                          tok >= 0 && tok < min(Tb, t_end + 2));
     };
     bf16x8 aA[KK], aB[KK];
     load(aA, c_begin);                                       // lands while W1 is staged
