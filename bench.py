@@ -546,7 +546,9 @@ def main():
 
     # The cache build needs only select's outputs and k/v, and writes only the
     # cache: it runs on a second stream beside the attention, which leaves LDS,
-    # registers and HBM bandwidth to spare (the ABI allows this pairing).
+    # registers and HBM bandwidth to spare (the ABI allows this pairing).  Its
+    # background form copies the rows on a few workgroups, so that the copy does
+    # not crowd the attention's latency-bound phases with a burst of traffic.
     side_stream = torch.cuda.Stream()
 
     def prefill_staged():
@@ -558,7 +560,7 @@ def main():
         ev[2].record(stream)
         side_stream.wait_event(ev[2])
         with torch.cuda.stream(side_stream):
-            layer.prefill_build_cache(kp, vp, ws, cache0)
+            layer.prefill_build_cache_background(kp, vp, ws, cache0)
         layer.prefill_attend(qp, kp, vp, ws, out)
         ev[3].record(stream)
         stream.wait_stream(side_stream)

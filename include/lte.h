@@ -247,6 +247,15 @@ int lte_prefill_attend(const lte_config* cfg, int64_t T, const uint16_t* q, cons
 int lte_prefill_build_cache(const lte_config* cfg, int64_t T, const uint16_t* k,
                             const uint16_t* v, void* workspace, size_t workspace_bytes,
                             void* cache, void* stream);
+/* The same cache, bit for bit, with the row copy (about 2 x 67 MB at B=32,
+ * C=w=512, D=128) spread over 32 workgroups that each walk many slot groups:
+ * it draws little HBM bandwidth at a time, for callers that run it on a second
+ * stream beside lte_prefill_attend, whose latency-bound phases a full-rate copy
+ * slows.  On its own it takes several times longer than lte_prefill_build_cache.
+ * Arguments, ownership and errors as lte_prefill_build_cache. */
+int lte_prefill_build_cache_background(const lte_config* cfg, int64_t T, const uint16_t* k,
+                                       const uint16_t* v, void* workspace,
+                                       size_t workspace_bytes, void* cache, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Ingest one token per sequence (position t = pos).  Figure 2 caption of the

@@ -231,6 +231,20 @@ int lte_prefill_build_cache(const lte_config* cfg, int64_t T, const uint16_t* k,
                                          cache_view(sh, cache), hipStream_t(stream)));
 }
 
+int lte_prefill_build_cache_background(const lte_config* cfg, int64_t T, const uint16_t* k,
+                                       const uint16_t* v, void* workspace,
+                                       size_t workspace_bytes, void* cache, void* stream) {
+    LTE_TRY(check_cfg(cfg));
+    LTE_TRY(check_T(T));
+    if (!k || !v || !cache) return LTE_ERR_INVALID_ARG;
+    Shape sh = make_shape(*cfg);
+    LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
+    WsPtrs w = ws_ptrs(sh, T, workspace);
+    return hip_status(launch_build_cache(sh, T, nullptr, nullptr, k, v, w.scores, w.rank, w.thr,
+                                         cache_view(sh, cache), hipStream_t(stream),
+                                         kBackgroundCopyWgs));
+}
+
 int lte_prefill(const lte_config* cfg, int64_t T, const uint16_t* q, const uint16_t* k,
                 const uint16_t* v, const lte_cnn* cnn, const float* score_override, void* cache,
                 void* workspace, size_t workspace_bytes, uint16_t* out, void* stream) {

@@ -171,46 +171,50 @@ __global__ __launch_bounds__(256) void cache_meta_kernel(int Tmax, int Hkv, int 
 }
 
 // Copies K/V rows into the cache slots: sink, retained segment, ring.
-// grid.x covers (batch, KV head) x slot groups; one 16-byte chunk per thread.
+// Work items are (batch, KV head) x slot groups, one 16-byte chunk per thread;
+// the grid walks them with a stride (one item per workgroup when the grid
+// covers them all).
 __global__ __launch_bounds__(256) void cache_copy_kernel(int Tmax, int Hkv, int D, int s, int w,
-                                                         int C, int S, int slots_per_block,
+                                                         int C, int S, int slots_per_block, int nblk,
                                                          const int32_t* __restrict__ seq_lens,
                                                          ChunkView xv,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          CacheView c) {
     const int nsb = (S + slots_per_block - 1) / slots_per_block;
-    const int bg = blockIdx.x / nsb;
-    const int sb = blockIdx.x % nsb;
-    const int b = bg / Hkv;
-    const int g = bg % Hkv;
-    const int T = seq_len_of(seq_lens, b, Tmax);            // rows of this sequence
-    const bool warm = xv.warm != nullptr && xv.warm[b] != 0;
-    const int off = warm ? xv.tok_off[b] : 0;
-    const int Tn = T + off;                                  // tokens of the sequence
-    const int chunks = D / 8;
-    const int cnt = c.count[bg];
-    for (int x = threadIdx.x; x < slots_per_block * chunks; x += blockDim.x) {
-        const int slot = sb * slots_per_block + x / chunks;
-        const int ch = x % chunks;
-        if (slot >= S) continue;
-        int j = -1;                                      // source row
-        if (slot < s) {
-            if (slot < T) j = slot;
-        } else if (slot < s + C) {
-            if (slot - s < cnt)
-                j = xv.seg_row != nullptr ? xv.seg_row[long(bg) * C + (slot - s)]
-                                          : c.ret_idx[long(bg) * C + (slot - s)];
-        } else {
-            const int rs = slot - s - C;
-            const int jj = Tn - 1 - ((Tn - 1 - rs) % w + w) % w;   // token
-            if (jj >= 0) j = jj - off;
+    for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int bg = blk / nsb;
+        const int sb = blk % nsb;
+        const int b = bg / Hkv;
+        const int g = bg % Hkv;
+        const int T = seq_len_of(seq_lens, b, Tmax);            // rows of this sequence
+        const bool warm = xv.warm != nullptr && xv.warm[b] != 0;
+        const int off = warm ? xv.tok_off[b] : 0;
+        const int Tn = T + off;                                  // tokens of the sequence
+        const int chunks = D / 8;
+        const int cnt = c.count[bg];
+        for (int x = threadIdx.x; x < slots_per_block * chunks; x += blockDim.x) {
+            const int slot = sb * slots_per_block + x / chunks;
+            const int ch = x % chunks;
+            if (slot >= S) continue;
+            int j = -1;                                      // source row
+            if (slot < s) {
+                if (slot < T) j = slot;
+            } else if (slot < s + C) {
+                if (slot - s < cnt)
+                    j = xv.seg_row != nullptr ? xv.seg_row[long(bg) * C + (slot - s)]
+                                              : c.ret_idx[long(bg) * C + (slot - s)];
+            } else {
+                const int rs = slot - s - C;
+                const int jj = Tn - 1 - ((Tn - 1 - rs) % w + w) % w;   // token
+                if (jj >= 0) j = jj - off;
+            }
+            if (j < 0) continue;
+            const long src = ((long(b) * Tmax + j) * Hkv + g) * D + ch * 8;
+            const long dst = (long(bg) * S + slot) * D + ch * 8;
+            *reinterpret_cast<uint4*>(c.k + dst) = *reinterpret_cast<const uint4*>(k + src);
+            *reinterpret_cast<uint4*>(c.v + dst) = *reinterpret_cast<const uint4*>(v + src);
         }
-        if (j < 0) continue;
-        const long src = ((long(b) * Tmax + j) * Hkv + g) * D + ch * 8;
-        const long dst = (long(bg) * S + slot) * D + ch * 8;
-        *reinterpret_cast<uint4*>(c.k + dst) = *reinterpret_cast<const uint4*>(k + src);
-        *reinterpret_cast<uint4*>(c.v + dst) = *reinterpret_cast<const uint4*>(v + src);
     }
 }
 
@@ -229,7 +233,7 @@ hipError_t launch_cache_init(const Shape& sh, const CacheView& cache, hipStream_
 hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_lens,
                               const ChunkView* chunk, const uint16_t* k, const uint16_t* v,
                               const float* scores, const int32_t* rank, const int32_t* thr,
-                              const CacheView& cache, hipStream_t st) {
+                              const CacheView& cache, hipStream_t st, int copy_wgs) {
     const int BG = sh.B * sh.Hkv;
     const ChunkView x = chunk ? *chunk : ChunkView{};
     hipLaunchKernelGGL(cache_meta_kernel, dim3(BG), dim3(256), 0, st, int(T), sh.Hkv, sh.s, sh.w,
@@ -238,8 +242,10 @@ hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_len
     if (e != hipSuccess) return e;
     const int spb = 32;                                  // slots per workgroup
     const int nsb = (sh.S + spb - 1) / spb;
-    hipLaunchKernelGGL(cache_copy_kernel, dim3(unsigned(long(BG) * nsb)), dim3(256), 0, st,
-                       int(T), sh.Hkv, sh.D, sh.s, sh.w, sh.C, sh.S, spb, seq_lens, x, k, v,
+    const int nblk = BG * nsb;
+    const int grid = (copy_wgs > 0 && copy_wgs < nblk) ? copy_wgs : nblk;
+    hipLaunchKernelGGL(cache_copy_kernel, dim3(unsigned(grid)), dim3(256), 0, st,
+                       int(T), sh.Hkv, sh.D, sh.s, sh.w, sh.C, sh.S, spb, nblk, seq_lens, x, k, v,
                        cache);
     return hipGetLastError();
 }

@@ -216,11 +216,15 @@ hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const int32_t* seq_
                                  const int32_t* q_lo, int q_rows, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const int32_t* rank,
                                  const int32_t* thr, uint16_t* out, hipStream_t st);
-// chunk (or null): the rows are a chunked prefill's extended sequence.
+// chunk (or null): the rows are a chunked prefill's extended sequence.  copy_wgs > 0
+// caps the row copy's grid at that many workgroups (each then walks several slot
+// groups); 0 gives every slot group its own workgroup.
 hipError_t launch_build_cache(const Shape& sh, int64_t T, const int32_t* seq_lens,
                               const ChunkView* chunk, const uint16_t* k, const uint16_t* v,
                               const float* scores, const int32_t* rank, const int32_t* thr,
-                              const CacheView& cache, hipStream_t st);
+                              const CacheView& cache, hipStream_t st, int copy_wgs = 0);
+// Workgroups of the row copy when the cache is built beside the prefill attention.
+constexpr int kBackgroundCopyWgs = 32;
 // Linear-attention layer: q, k, v [B][T][H][D] bf16, log_a [B][T][H] fp32,
 // states [B][H][D][D] fp32 (S[dv][dk]); state_in may be null (zero state) and
 // may equal state_out.

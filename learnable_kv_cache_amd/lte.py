@@ -83,6 +83,7 @@ SIGNATURES = {
     "lte_prefill_select": (ctypes.c_int, [_CFG, _I64, _P, _P, _SZ, _P]),
     "lte_prefill_attend": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _P, _SZ, _P, _P]),
     "lte_prefill_build_cache": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _SZ, _P, _P]),
+    "lte_prefill_build_cache_background": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _SZ, _P, _P]),
     "lte_score_evict": (ctypes.c_int, [_CFG, _CNNP, _P, _P, _P, _P]),
     "lte_decode_attend": (ctypes.c_int, [_CFG, _P, _P, _P, _SZ, _P, _P]),
     "lte_decode_step": (ctypes.c_int, [_CFG, _P, _P, _P, _CNNP, _P, _P, _SZ, _P, _P]),
@@ -273,6 +274,14 @@ class Layer:
         _check(lib().lte_prefill_build_cache(ctypes.byref(self._c), int(T), _ptr(k), _ptr(v),
                                              _ptr(workspace), int(workspace.numel()),
                                              _ptr(cache), _stream()), "lte_prefill_build_cache")
+
+    def prefill_build_cache_background(self, k, v, workspace, cache):
+        """prefill_build_cache with a low-bandwidth row copy, for a second stream beside
+        prefill_attend."""
+        T = k.shape[1]
+        _check(lib().lte_prefill_build_cache_background(
+            ctypes.byref(self._c), int(T), _ptr(k), _ptr(v), _ptr(workspace),
+            int(workspace.numel()), _ptr(cache), _stream()), "lte_prefill_build_cache_background")
 
     def workspace_views(self, workspace, T: int) -> dict:
         """Device views of the last prefill's scores [B,Hkv,T], rank, thr, ncand."""

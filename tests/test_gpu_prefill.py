@@ -217,14 +217,19 @@ def test_repeat_runs_are_bitwise_identical_full_size():
     assert torch.equal(ca, cb)
 
 
-def test_attend_beside_cache_build_matches_serial_prefill():
+@pytest.mark.parametrize("wl_id,T,B", [(1, None, None), (3, 2048, 2)],
+                         ids=["tiny", "B2T2048"])
+@pytest.mark.parametrize("background", [False, True], ids=["full_copy", "background_copy"])
+def test_attend_beside_cache_build_matches_serial_prefill(wl_id, T, B, background):
     """After select, attend and the cache build share only read-only inputs: run on two
-    streams at once they give the serial prefill's output and cache bit for bit."""
-    inp = synth.workload_inputs(1)
+    streams at once they give the serial prefill's output and cache bit for bit.  The
+    background build (32 copy workgroups, each walking many slot groups at B2 T2048:
+    8 (b, g) x 33 slot groups) builds the same cache."""
+    inp = synth.workload_inputs(wl_id, T=T, B=B, decode_steps=0)
     wl = inp["workload"]
     T = inp["T"]
-    q, k, v = (_dev(x) for x in (inp["q"], inp["k"], inp["v"]))
-    layer = lte.Layer(lte.Config(wl.B, wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window, wl.capacity))
+    q, k, v = (_dev(x[:, :T]) for x in (inp["q"], inp["k"], inp["v"]))
+    layer = lte.Layer(lte.Config(inp["B"], wl.Hq, wl.Hkv, wl.D, wl.sink, wl.window, wl.capacity))
     cnn = lte.CNN(inp["cnn"])
     ws = layer.alloc_workspace(T)
 
@@ -246,7 +251,10 @@ def test_attend_beside_cache_build_matches_serial_prefill():
     done.record(main)
     side.wait_event(done)
     with torch.cuda.stream(side):
-        layer.prefill_build_cache(k, v, ws, cache_b)
+        if background:
+            layer.prefill_build_cache_background(k, v, ws, cache_b)
+        else:
+            layer.prefill_build_cache(k, v, ws, cache_b)
     layer.prefill_attend(q, k, v, ws, out_b)
     main.wait_stream(side)
     torch.cuda.synchronize()
