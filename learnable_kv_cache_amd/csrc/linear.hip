@@ -67,6 +67,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     __shared__ __align__(16) u32x4 Ws[kChunk * CPR];     // w_j K[j]
     __shared__ __align__(16) u32x4 Ps[kChunk * 8];       // P[t][j] bf16
     __shared__ __align__(16) u32x4 Sb[KK * 2 * D];       // S^T as bf16 k operands
+    __shared__ __align__(16) uint16_t Os[kChunk * D];     // the chunk's outputs, bf16 rows
     __shared__ __align__(16) float Gb[2][kChunk];         // G_t (two chunks)
     __shared__ __align__(16) float Eb[2][kChunk];         // exp(G_t)
     const int tid = threadIdx.x;
@@ -195,8 +196,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     scan_g(0);
     share_state();
     __syncthreads();
-    // this chunk's outputs are stored after the next chunk's rows are stashed, so that
-    // the wait for those loads never covers these stores
+    // a chunk's outputs go through LDS and leave as whole rows after the chunk's last
+    // barrier, ahead of the next chunk's loads
+    constexpr int LPO = kChunk * CPR / NT;               // 16-byte output pieces per thread
     uint16_t opend[16];
     for (int ch = 0; ch < nchunk; ++ch) {
         const int t0 = ch * kChunk;
@@ -300,7 +302,6 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
             // element e: row t = tt*32 + (e/4)*8 + h*4 + e%4, dim 32*wave + lane&31
-            uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D + dcol;
             float4 ev[4];                                 // exp(G_t) of this lane's rows
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
@@ -310,7 +311,6 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
                 const float e4v[4] = {ev[e >> 2].x, ev[e >> 2].y, ev[e >> 2].z, ev[e >> 2].w};
                 opend[e] = __builtin_bit_cast(uint16_t, (__bf16)(oi[e] + e4v[e & 3] * ox[e]));
             }
-            (void)ob;
         }
         // ---- S^T = exp(G_last) S^T + (w K)^T V for this wave's state tiles ------------
         const float decay = __expf(g_last);
@@ -325,18 +325,27 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
         }
         if (ch + 1 < nchunk) scan_g((ch + 1) & 1);       // the next chunk's G, other buffer
         __syncthreads();                                  // the chunk's tiles and Sb are free
+        // element e: row t = xw*32 + (e/4)*8 + h*4 + e%4, dim 32 dw + lane&31
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int t = xw * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+            Os[t * D + dcol] = opend[e];
+        }
         if (ch + 1 < nchunk) {
             stash();
             share_state();
-            __syncthreads();
         }
+        __syncthreads();
         {
-            // element e: row t = xw*32 + (e/4)*8 + h*4 + e%4, dim 32 dw + lane&31
-            uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D + dcol;
+            uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int t = xw * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                if (nrow == kChunk || t < nrow) ob[long(t) * rs] = opend[e];
+            for (int u = 0; u < LPO; ++u) {
+                const int x = tid + u * NT;
+                const int r = x / CPR;
+                const int c = x % CPR;
+                if (r < nrow)
+                    *reinterpret_cast<u32x4*>(ob + long(r) * rs + c * 8) =
+                        *reinterpret_cast<const u32x4*>(&Os[r * D + c * 8]);
             }
         }
     }
