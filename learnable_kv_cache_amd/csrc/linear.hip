@@ -18,7 +18,10 @@
 // 2 D/32 waves, two per SIMD: wave w takes dims [32 dw, 32 dw + 32), dw = w/2,
 // of the output rows [32 x, 32 x + 32), x = w%2, and the S^T tiles kt of its
 // dims with kt in [x D/64, (x+1) D/64); the state is shared as bf16 through
-// LDS for the inter-chunk product.  An MFMA
+// LDS for the inter-chunk product.  Two barriers per chunk: q and k are
+// double-buffered, so the next chunk's are stored before the second barrier;
+// its v and the state copy, which it reads only after its first barrier, after
+// the second.  An MFMA
 // accumulator holds its column in lane & 31 and rows (e/4)*8 + (lane/32)*4 +
 // e%4; read as a 16-wide k operand, element i of lane-half h is then row
 // 16c + (i<4 ? 4h + i : 8 + 4h + i-4) of step c, and every other operand is
@@ -61,8 +64,12 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int KK = D / 16;              // k-steps over D
     constexpr int KTW = DT / 2;             // state tiles per wave
-    __shared__ __align__(16) u32x4 Qs[kChunk * CPR];
-    __shared__ __align__(16) u32x4 Ks[kChunk * CPR];
+    // q and k tiles double-buffered: the next chunk's are stored before the chunk's last
+    // barrier, while its own are still read
+    __shared__ __align__(16) u32x4 Qs0[kChunk * CPR];
+    __shared__ __align__(16) u32x4 Ks0[kChunk * CPR];
+    __shared__ __align__(16) u32x4 Qs1[kChunk * CPR];
+    __shared__ __align__(16) u32x4 Ks1[kChunk * CPR];
     __shared__ __align__(16) u32x4 Vs[kChunk * CPR];
     __shared__ __align__(16) u32x4 Ws[kChunk * CPR];     // w_j K[j]
     __shared__ __align__(16) u32x4 Ps[kChunk * 8];       // P[t][j] bf16
@@ -174,9 +181,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             Eb[gbuf][lane] = __expf(g);
         }
     };
-    auto stash = [&]() {
-        // the LDS offsets are recomputed here on every call: hoisted out of the chunk
-        // loop they were spilled, and their reloads serialised the stores
+    // the LDS offsets are recomputed on every call: hoisted out of the chunk loop they
+    // were spilled, and their reloads serialised the stores
+    auto stash_qk = [&](u32x4* Qd, u32x4* Kd) __attribute__((always_inline)) {
         int tx = tid;
         asm volatile("" : "+v"(tx));
 #pragma unroll
@@ -184,15 +191,26 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             const int x = tx + u * NT;
             const int r = x / CPR;
             const int c = x % CPR;
-            Qs[r * CPR + (c ^ rswz<D>(r))] = pq[u];
-            Ks[r * CPR + (c ^ rswz<D>(r))] = pk[u];
+            Qd[r * CPR + (c ^ rswz<D>(r))] = pq[u];
+            Kd[r * CPR + (c ^ rswz<D>(r))] = pk[u];
+        }
+    };
+    auto stash_v = [&]() __attribute__((always_inline)) {
+        int tx = tid;
+        asm volatile("" : "+v"(tx));
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int x = tx + u * NT;
+            const int r = x / CPR;
+            const int c = x % CPR;
             Vs[r * CPR + (c ^ tswz<D>(r))] = pv[u];
         }
     };
 
     const int nchunk = (T + kChunk - 1) / kChunk;
     fetch(0);
-    stash();
+    stash_qk(Qs0, Ks0);
+    stash_v();
     scan_g(0);
     share_state();
     __syncthreads();
@@ -201,6 +219,10 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     constexpr int LPO = kChunk * CPR / NT;               // 16-byte output pieces per thread
     uint16_t opend[16];
     for (int ch = 0; ch < nchunk; ++ch) {
+        const u32x4* Qs = (ch & 1) ? Qs1 : Qs0;
+        const u32x4* Ks = (ch & 1) ? Ks1 : Ks0;
+        u32x4* QN = (ch & 1) ? Qs0 : Qs1;
+        u32x4* KN = (ch & 1) ? Ks0 : Ks1;
         const int t0 = ch * kChunk;
         const int nrow = min(kChunk, T - t0);
         if (ch + 1 < nchunk) fetch(t0 + kChunk);          // in flight during this chunk
@@ -324,18 +346,19 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             }
         }
         if (ch + 1 < nchunk) scan_g((ch + 1) & 1);       // the next chunk's G, other buffer
-        __syncthreads();                                  // the chunk's tiles and Sb are free
         // element e: row t = xw*32 + (e/4)*8 + h*4 + e%4, dim 32 dw + lane&31
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int t = xw * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
             Os[t * D + dcol] = opend[e];
         }
+        if (ch + 1 < nchunk) stash_qk(QN, KN);           // the other q, k buffers
+        __syncthreads();                                  // the chunk's tiles and Sb are free
+        // the next chunk reads v and Sb only after its first barrier
         if (ch + 1 < nchunk) {
-            stash();
+            stash_v();
             share_state();
         }
-        __syncthreads();
         {
             uint16_t* ob = out + (long(b) * T + t0) * rs + long(h) * D;
 #pragma unroll
