@@ -214,7 +214,7 @@ int lte_prefill_attend(const lte_config* cfg, int64_t T, const uint16_t* q, cons
     LTE_TRY(check_ws(sh, T, workspace, workspace_bytes));
     WsPtrs w = ws_ptrs(sh, T, workspace);
     return hip_status(
-        launch_attend_prefill(sh, T, nullptr, nullptr, 0, q, k, v, w.rank, w.thr, out,
+        launch_attend_prefill(sh, T, nullptr, nullptr, 0, q, k, v, w.rank, w.thr, w.ncand, out,
                               hipStream_t(stream)));
 }
 
@@ -288,7 +288,8 @@ int lte_prefill_varlen(const lte_config* cfg, int64_t T, const int32_t* seq_lens
     LTE_TRY(hip_status(
         launch_select(sh, T, seq_lens, sc, w.rank, w.thr, w.ncand, w.select_scratch, st)));
     LTE_TRY(hip_status(
-        launch_attend_prefill(sh, T, seq_lens, nullptr, 0, q, k, v, w.rank, w.thr, out, st)));
+        launch_attend_prefill(sh, T, seq_lens, nullptr, 0, q, k, v, w.rank, w.thr, w.ncand, out,
+                              st)));
     if (cache != nullptr)
         LTE_TRY(hip_status(launch_build_cache(sh, T, seq_lens, nullptr, k, v, w.scores, w.rank, w.thr,
                                              cache_view(sh, cache), st)));
@@ -335,7 +336,7 @@ int lte_prefill_chunk(const lte_config* cfg, int64_t n, const uint16_t* q, const
     LTE_TRY(hip_status(
         launch_select(sh, E, x.ext_len, w.scores, w.rank, w.thr, w.ncand, w.select_scratch, st)));
     LTE_TRY(hip_status(launch_attend_prefill(sh, E, x.ext_len, x.q_lo, int(n), q, ek, ev, w.rank,
-                                             w.thr, out, st)));
+                                             w.thr, w.ncand, out, st)));
     return hip_status(
         launch_build_cache(sh, E, x.ext_len, &x, ek, ev, w.scores, w.rank, w.thr, c, st));
 }

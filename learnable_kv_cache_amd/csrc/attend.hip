@@ -103,7 +103,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const int32_t* __restrict__ q_lo, int q_rows, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ thr,
-    uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ ncand, uint16_t* __restrict__ out) {
     constexpr int NW = 8;                   // waves
     constexpr int P = NW * 32 / G;          // positions per tile
     constexpr int KK = D / 16;              // MFMA k-steps of q.k
@@ -160,6 +160,10 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     const int nband = (band_hi - band_lo + 1 + 63) / 64;
     const int32_t* rk = rank + long(bg) * T;
     const int32_t* th = thr + long(bg) * T;
+    // a (b, g) without candidates retains nothing: its ranks are not read and the
+    // gathered list is the sink alone
+    const bool has_cand = !(ncand != nullptr && ncand[bg] == 0);
+    const int scan_hi = has_cand ? band_lo : s;
     // key rows of this (batch, KV head): byte offsets fit 32 bits (T * Hkv * D
     // * 2 < 2^31 is checked on the host) and row * kv_bytes fits 24-bit factors
     const char* kbytes = reinterpret_cast<const char*>(k + (long(b) * T * Hkv + g) * D);
@@ -225,14 +229,14 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     int brv = kNotCand;
     if (tid < kBr) {
         const int j = band_lo + tid;
-        brv = (j < s) ? -1 : ((j <= band_hi) ? rk[j] : kNotCand);    // sink always passes
+        brv = (j < s) ? -1 : ((j <= band_hi && has_cand) ? rk[j] : kNotCand);   // sink always passes
     }
     // list candidates j = s + u*NT + tid of the first pass (coalesced)
     int rr[LU];
 #pragma unroll
     for (int u = 0; u < LU; ++u) {
         const int j = s + u * NT + tid;
-        rr[u] = (j < band_lo) ? rk[j] : kNotCand;
+        rr[u] = (j < scan_hi) ? rk[j] : kNotCand;
     }
 
     const int thr_row = (irow - w >= 0) ? th[irow - w] : -2;
@@ -258,12 +262,12 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
     int ntr = 0;                                  // transient entries so far
     int par = 0;                                  // count buffer of this pass
     for (int j = tid; j < ns; j += NT) lst[j] = uint32_t(j);           // field 0: always visible
-    for (int base = s; base < band_lo; base += LU * NT) {
+    for (int base = s; base < scan_hi; base += LU * NT) {
         if (base != s) {
 #pragma unroll
             for (int u = 0; u < LU; ++u) {
                 const int j = base + u * NT + tid;
-                rr[u] = (j < band_lo) ? rk[j] : kNotCand;
+                rr[u] = (j < scan_hi) ? rk[j] : kNotCand;
             }
         }
         uint32_t pre[LU];
@@ -598,7 +602,7 @@ template <int D>
 hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens,
                            const int32_t* q_lo, int q_rows, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const int32_t* rank, const int32_t* thr,
-                           uint16_t* out, hipStream_t st) {
+                           const int32_t* ncand, uint16_t* out, hipStream_t st) {
     const int G = sh.G;
     const int P = 256 / G;
     const int ntile = int((T + P - 1) / P);
@@ -607,8 +611,7 @@ hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens,
     case GG:                                                                                  \
         hipLaunchKernelGGL((attend_prefill_kernel<D, GG>), grid, dim3(512), 0, st, int(T),    \
                            sh.Hq, sh.Hkv, sh.s, sh.w, ntile, seq_lens, q_lo, q_rows, q, k, v, \
-                           rank, thr,                                                        \
-                           out);                                                              \
+                           rank, thr, ncand, out);                                           \
         break;
     switch (G) {
         LTE_ATTEND_CASE(1)
@@ -628,10 +631,12 @@ hipError_t launch_attend_d(const Shape& sh, int64_t T, const int32_t* seq_lens,
 hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
                                  const int32_t* q_lo, int q_rows, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const int32_t* rank,
-                                 const int32_t* thr, uint16_t* out, hipStream_t st) {
+                                 const int32_t* thr, const int32_t* ncand, uint16_t* out,
+                                 hipStream_t st) {
     if (sh.D == 128)
-        return launch_attend_d<128>(sh, T, seq_lens, q_lo, q_rows, q, k, v, rank, thr, out, st);
-    return launch_attend_d<64>(sh, T, seq_lens, q_lo, q_rows, q, k, v, rank, thr, out, st);
+        return launch_attend_d<128>(sh, T, seq_lens, q_lo, q_rows, q, k, v, rank, thr, ncand, out,
+                                    st);
+    return launch_attend_d<64>(sh, T, seq_lens, q_lo, q_rows, q, k, v, rank, thr, ncand, out, st);
 }
 
 }  // namespace lte

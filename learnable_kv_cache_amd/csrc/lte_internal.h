@@ -211,11 +211,13 @@ hipError_t launch_select(const Shape& sh, int64_t T, const int32_t* seq_lens, co
                          int32_t* rank, int32_t* thr, int32_t* ncand, uint32_t* scratch,
                          hipStream_t st);
 // q_lo (device, [B], or null): only rows >= q_lo[b] are queries; q and out are
-// then [B][q_rows][Hq][D] with row i at i - q_lo[b].
+// then [B][q_rows][Hq][D] with row i at i - q_lo[b].  ncand (device, [B][Hkv], or
+// null): the selection's candidate counts; a (b, g) with none skips its rank scan.
 hipError_t launch_attend_prefill(const Shape& sh, int64_t T, const int32_t* seq_lens,
                                  const int32_t* q_lo, int q_rows, const uint16_t* q,
                                  const uint16_t* k, const uint16_t* v, const int32_t* rank,
-                                 const int32_t* thr, uint16_t* out, hipStream_t st);
+                                 const int32_t* thr, const int32_t* ncand, uint16_t* out,
+                                 hipStream_t st);
 // chunk (or null): the rows are a chunked prefill's extended sequence.  copy_wgs > 0
 // caps the row copy's grid at that many workgroups (each then walks several slot
 // groups); 0 gives every slot group its own workgroup.
