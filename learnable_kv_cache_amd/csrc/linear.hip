@@ -157,12 +157,11 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
             const int x = tid + u * NT;
             const int r = x / CPR;
             const int c = x % CPR;
-            pq[u] = pk[u] = pv[u] = u32x4{0u, 0u, 0u, 0u};
+            pq[u] = pk[u] = u32x4{0u, 0u, 0u, 0u};
             if (r < nr) {
                 const long src = (long(b) * T + c0 + r) * rs + long(h) * D + c * 8;
                 pq[u] = *reinterpret_cast<const u32x4*>(q + src);
                 pk[u] = *reinterpret_cast<const u32x4*>(k + src);
-                pv[u] = *reinterpret_cast<const u32x4*>(v + src);
             }
         }
         if (wave == NW - 1) pg = (lane < nr) ? log_a[(long(b) * T + c0 + lane) * H + h] : 0.0f;
@@ -208,7 +207,21 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     };
 
     const int nchunk = (T + kChunk - 1) / kChunk;
+    auto fetch_v = [&](int c0) {
+        const int nr = min(kChunk, T - c0);
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int x = tid + u * NT;
+            const int r = x / CPR;
+            const int c = x % CPR;
+            pv[u] = u32x4{0u, 0u, 0u, 0u};
+            if (r < nr)
+                pv[u] = *reinterpret_cast<const u32x4*>(v + (long(b) * T + c0 + r) * rs +
+                                                        long(h) * D + c * 8);
+        }
+    };
     fetch(0);
+    fetch_v(0);
     stash_qk(Qs0, Ks0);
     stash_v();
     scan_g(0);
@@ -289,6 +302,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
         }
         __syncthreads();
 
+        if (ch + 1 < nchunk) fetch_v(t0 + kChunk);       // needed after the second barrier
         // ---- V operands of this wave's dims, k-steps c = 0..3 (P V and the update) ----
         bf16x8 vop[4];
 #pragma unroll
