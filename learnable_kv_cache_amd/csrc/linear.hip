@@ -170,12 +170,16 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
     // G buffer gbuf
     auto scan_g = [&](int gbuf) {
         if (wave == NW - 1) {
+            // inclusive prefix sum over the wave by DPP moves: shifts by 1, 2, 4, 8 within
+            // rows of 16 lanes, then each row's last lane into the rows after it; a lane
+            // whose source is out of range adds the +0.0 passed as the old value
             float g = fmaxf(pg, kLogAMin);
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float y = __shfl_up(g, d, 64);
-                if (lane >= d) g += y;
-            }
+            g += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(g), 0x111, 0xf, 0xf, false));
+            g += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(g), 0x112, 0xf, 0xf, false));
+            g += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(g), 0x114, 0xf, 0xf, false));
+            g += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(g), 0x118, 0xf, 0xf, false));
+            g += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(g), 0x142, 0xa, 0xf, false));
+            g += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(g), 0x143, 0xc, 0xf, false));
             Gb[gbuf][lane] = g;
             Eb[gbuf][lane] = __expf(g);
         }
