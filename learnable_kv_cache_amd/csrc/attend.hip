@@ -287,12 +287,7 @@ __global__ __launch_bounds__(512) void attend_prefill_kernel(
         // second barrier; the counts alternate between two buffers, so the next
         // pass's writes wait only for its own barrier
         const int c = wcnt[par][lane];
-        int incl = c;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += y;
-        }
+        const int incl = wave_incl_sum(c);
         const int excl = incl - c;
         const int tot = __builtin_amdgcn_readlane(incl, 63);
 #pragma unroll

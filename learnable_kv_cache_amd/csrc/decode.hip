@@ -111,6 +111,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float* p) {
     return __builtin_amdgcn_make_buffer_rsrc(p, 0, 0x7fffffff, 0x00020000);
 }
 
+// Max and sum of a value over the four lanes l, l ^ 16, l ^ 32, l ^ 48, by the two
+// row-swapping permutes (each lane takes the larger, or the sum, of the pair it
+// holds afterwards: its own value and its partner's), with no LDS round trip.
+__device__ __forceinline__ float max_swap(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float add_swap(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Decision for the token leaving at the ingest of position t, from the state
 // after the previous step: -2 unscored, -1 not kept, else its segment slot.
 __device__ __forceinline__ int decide_slot(int64_t t, float rl, int cnt, int weak,
@@ -592,8 +612,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
         }
         float mc = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                          fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-        mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
-        mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+        mc = max_swap(mc);
         // NaN (both -inf: nothing visible yet) compares false: no move
         const bool move = (mc - m_ref) * csc > 8.0f;
         if (__ballot(move) != 0ull) {
@@ -653,8 +672,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_step_kernel(
             consume(e_hi - 1, Kx, Vx, -1);
         }
     }
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = add_swap(l_run);
     // ---- this step's share of the deferred batch (wave-private LDS) ----------------------
     if (INGEST && t == u + w - 3) {
         __builtin_amdgcn_s_waitcnt(0);

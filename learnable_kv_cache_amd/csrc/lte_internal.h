@@ -28,7 +28,23 @@ constexpr int kMaxCapacity = 4096;
 constexpr int64_t kMaxT = 32768;     // the selection sort keeps <= 32 keys per thread
 constexpr int64_t kMaxLinearT = int64_t(1) << 22;   // linear layer: tokens per call
 constexpr int32_t kNotCand = 0x7fffffff;   // rank of a non-candidate
+
 constexpr int32_t kAllPass = 0x7ffffffe;   // thr when every candidate is kept
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4
+// and 8 within each row of 16 lanes, then each row's last lane is added into the rows
+// after it (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).  Lanes
+// whose source is out of range add the 0 passed as the old value.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+    return x;
+}
+
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

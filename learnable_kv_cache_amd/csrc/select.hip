@@ -64,20 +64,6 @@ __device__ __forceinline__ unsigned long long same_digit(int d, bool valid, uint
     return __ballot(valid) & ~((static_cast<unsigned long long>(dhi) << 32) | dlo);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4
-// and 8 within each row of 16 lanes, then each row's last lane is added into the rows
-// after it (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).  Lanes
-// whose source is out of range add the 0 passed as the old value.
-__device__ __forceinline__ int wave_incl_sum(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
-    return x;
-}
-
 // OR of a value over the wave, by the same DPP pattern (lane 63 ends with all lanes).
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
     int x = int(v);
