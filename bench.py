@@ -551,18 +551,26 @@ def main():
     # not crowd the attention's latency-bound phases with a burst of traffic.
     side_stream = torch.cuda.Stream()
 
-    def prefill_staged():
+    # Instrumented, the prefill records events between its stages (the per-stage times);
+    # otherwise only at its ends (the prefill time), since each timing event adds a
+    # few microseconds to the stream.
+    def prefill_staged(instrumented=True):
         gate()
         ev[0].record(stream)
         layer.prefill_score(kp, vp, cnn, ws)
-        ev[1].record(stream)
+        if instrumented:
+            ev[1].record(stream)
         layer.prefill_select(T, ws)
-        ev[2].record(stream)
-        side_stream.wait_event(ev[2])
+        if instrumented:
+            ev[2].record(stream)
+            side_stream.wait_event(ev[2])
+        else:
+            side_stream.wait_stream(stream)
         with torch.cuda.stream(side_stream):
             layer.prefill_build_cache_background(kp, vp, ws, cache0)
         layer.prefill_attend(qp, kp, vp, ws, out)
-        ev[3].record(stream)
+        if instrumented:
+            ev[3].record(stream)
         stream.wait_stream(side_stream)
         ev[4].record(stream)
 
@@ -602,9 +610,12 @@ def main():
         flush_buf = torch.empty(2 * MALL_BYTES, dtype=torch.uint8, device=dev)
     for it in range(args.warmup + args.steps):
         timed = it >= args.warmup
+        # timed steps alternate: the prefill time from uninstrumented prefills, the
+        # stage times from instrumented ones (each step runs one prefill either way)
+        instrumented = (it - args.warmup) % 2 == 1 or args.steps == 1
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        prefill_staged()
+        prefill_staged(instrumented)
         if not args.no_decode:
             # every decode replay starts from this prefill's cache (positions T .. T+ndec-1),
             # untimed: the rotating caches are re-seeded, then the last-level cache is
@@ -624,11 +635,13 @@ def main():
         t1 = time.perf_counter()
         if timed:
             step_ms.append((t1 - t0) * 1e3)
-            stage_ms["score"].append(ev[0].elapsed_time(ev[1]))
-            stage_ms["select"].append(ev[1].elapsed_time(ev[2]))
-            stage_ms["attend"].append(ev[2].elapsed_time(ev[3]))
-            stage_ms["build_cache"].append(ev[3].elapsed_time(ev[4]))
-            prefill_ms.append(ev[0].elapsed_time(ev[4]))
+            if instrumented:
+                stage_ms["score"].append(ev[0].elapsed_time(ev[1]))
+                stage_ms["select"].append(ev[1].elapsed_time(ev[2]))
+                stage_ms["attend"].append(ev[2].elapsed_time(ev[3]))
+                stage_ms["build_cache"].append(ev[3].elapsed_time(ev[4]))
+            if not instrumented or args.steps == 1:
+                prefill_ms.append(ev[0].elapsed_time(ev[4]))
             if not args.no_decode:
                 dec_rot_ms.append(dev_ev[0].elapsed_time(dev_ev[1]))
                 dec_warm_ms.append(dev_ev[2].elapsed_time(dev_ev[3]))
