@@ -145,8 +145,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void linear_prefill_kernel(
         return a;
     };
 
-    // ---- chunk loads: fetched into registers one chunk ahead, stored to LDS at the
-    //      chunk boundary (q, k, v rows zero past T; log a clamped, zero past T) ------
+    // ---- chunk loads, one chunk ahead into registers: q, k (and log a) at a chunk's
+    //      top, stored to LDS before its second barrier; v after its first barrier,
+    //      stored after its second (rows zero past T; log a clamped, zero past T) -----
     constexpr int LPT = kChunk * CPR / NT;               // 16-byte pieces per thread
     u32x4 pq[LPT], pk[LPT], pv[LPT];
     float pg = 0.0f;

@@ -28,7 +28,6 @@ constexpr int kMaxCapacity = 4096;
 constexpr int64_t kMaxT = 32768;     // the selection sort keeps <= 32 keys per thread
 constexpr int64_t kMaxLinearT = int64_t(1) << 22;   // linear layer: tokens per call
 constexpr int32_t kNotCand = 0x7fffffff;   // rank of a non-candidate
-
 constexpr int32_t kAllPass = 0x7ffffffe;   // thr when every candidate is kept
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4
@@ -44,7 +43,6 @@ __device__ __forceinline__ int wave_incl_sum(int x) {
     x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
     return x;
 }
-
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
