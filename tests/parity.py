@@ -91,3 +91,38 @@ def output_errors(o_gpu: np.ndarray, o_ref: np.ndarray):
 
 MAX_ABS = 2e-2      # bf16 inputs/outputs, fp32 accumulation
 MEAN_ABS = 1e-3
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """x rounded to bfloat16 (round to nearest even), returned as float64."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.bfloat16).double().numpy()
+
+
+def spiked_keys(k, every: int, top: float):
+    """k (bf16 [B, T, Hkv, D]) with the rows of every ``every``-th token scaled by a factor
+    growing linearly from 1 at token 0 to ``top`` at token T-1, rounded to bf16: later
+    keys carry ever larger logits (of either sign), so a query row keeps meeting keys that
+    beat everything it has seen so far."""
+    import torch
+    kk = k.float().clone()
+    T = kk.shape[1]
+    js = np.arange(0, T, every)
+    f = 1.0 + (top - 1.0) * js / max(T - 1, 1)
+    kk[:, js] *= torch.tensor(f, dtype=torch.float32)[None, :, None, None]
+    return kk.to(torch.bfloat16)
+
+
+def late_key_gain(q: np.ndarray, k: np.ndarray, w: int, rows) -> float:
+    """Largest, over the given rows (batch 0, query head 0, KV head 0), of the row's best
+    logit in its window minus its best logit over the first 32 keys of that window, in
+    log2 units: above 8, a kernel that walks the window from its oldest keys and keeps a
+    reference maximum must move that reference."""
+    D = q.shape[-1]
+    best = -np.inf
+    for i in rows:
+        lo = max(0, i - w + 1)
+        lg = (k[0, lo:i + 1, 0].astype(np.float64) @ q[0, i, 0].astype(np.float64)) / np.sqrt(D)
+        best = max(best, (lg.max() - lg[:32].max()) * np.log2(np.e))
+    return float(best)

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from learnable_kv_cache_amd import lte, synth
-from tests.parity import (MAX_ABS, MEAN_ABS, gpu_ends, keep_set_mismatches, normalize_ends,
-                          output_errors)
+from tests.parity import (MAX_ABS, MEAN_ABS, bf16_round, gpu_ends, keep_set_mismatches,
+                          late_key_gain, normalize_ends, output_errors, spiked_keys)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,6 +133,37 @@ def test_tied_scores_long_prompt_exact_sets(shape):
     rows = sorted(set(rng.integers(0, T, 48).tolist()) | {0, w, T - 1})
     pairs = [(b, g) for b in range(B) for g in range(Hkv)]
     _check_rows(q, k, v, s, w, ends_g, out, rows, pairs)
+
+
+@pytest.mark.parametrize("shape", [
+    # B, T, Hq, Hkv, D, s, w, C
+    (1, 700, 4, 1, 128, 4, 64, 40),
+    (2, 300, 8, 2, 64, 2, 40, 16),
+    (1, 600, 16, 1, 128, 4, 300, 100),
+], ids=lambda s: "B{}T{}Hq{}Hkv{}D{}s{}w{}C{}".format(*s))
+def test_growing_logits_move_the_reference(shape):
+    """Keys whose logits grow along the sequence: a row's later blocks (the diagonal's, then
+    the retained columns) keep beating its reference maximum by more than 2^8 in the
+    exponent, so the rebase (reference moved, running sum and output rescaled) runs again
+    and again, a path that inputs drawn from N(0, 1) never reach.  Every row against the
+    oracle.  Outputs dominated by one key have the magnitude of that key's v, whose bf16
+    rounding alone is about 1e-3 mean-abs, so the oracle's value is rounded to bf16, the
+    output's format, before the comparison."""
+    B, T, Hq, Hkv, D, s, w, C = shape
+    q, k, v = synth.make_qkv(B, T, Hq, Hkv, D, seed=301 + T)
+    k = spiked_keys(k, 7, 12.0)
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    assert late_key_gain(qn, kn, w, range(T // 2, T)) > 16.0
+    rng = np.random.default_rng(T + 1)
+    r = rng.uniform(0.2, 1.0, size=(B, Hkv, T)).astype(np.float32)
+    out, views, _, _ = run_prefill(B, T, Hq, Hkv, D, s, w, C, q, k, v, override=r)
+    ends_or = oracle.all_ends(r, s, w, C, T)
+    ends_g = _ends_all(views, w, T)
+    np.testing.assert_array_equal(normalize_ends(ends_g, w), normalize_ends(ends_or, w))
+    ref = bf16_round(oracle.attention(qn, kn, vn, s, w, ends_g))
+    assert np.isfinite(out).all()
+    mx, mean = output_errors(out, ref)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
 
 
 def _random_shape(seed):
